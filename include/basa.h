@@ -1,0 +1,168 @@
+/*
+ * basa.h -- C ABI of the shifted-window sparse attention library (gfx950).
+ *
+ * The library computes BASA-style attention for diffusion transformers:
+ * self-attention over the visual token grid of an image (2D) or video (3D)
+ * is replaced by dense attention inside non-overlapping local windows, the
+ * window partition is cyclically shifted from one DiT block to the next, and
+ * each window's keys may be extended by a global memory of mean-pooled K/V
+ * tokens under the same softmax.
+ *
+ * Sources (the web pages this library is written from):
+ *   [BASA-1] BASA forum summary, English mirror of "BASA: Backend-Agnostic
+ *            Sparse Attention for Fast High-Resolution Diffusion
+ *            Transformers" (zhichai.net), sections "Summary", "Overview",
+ *            "The BASA Method".
+ *   [BASA-2] BASA discussion reply (zhichai.net topic reply), paragraphs on
+ *            the method's four parts and on its complexity.
+ *   [SFA]    Scale-Free Attention abstract (artificialintelbulletin.com):
+ *            mean pooling, token-count correction, one shared softmax.
+ *
+ * Conventions shared by every call
+ *   - Plain C types only; device buffers are raw device pointers, shape and
+ *     geometry arrays are host pointers read during the call only.
+ *   - Tensors Q, K, V, O hold B x H x n x D elements with D contiguous and
+ *     the n tokens in raster order of the grid, idx = (t*Hg + y)*Wg + x.
+ *     layout BASA_LAYOUT_BHND: element (b,h,i,d) at ((b*H + h)*n + i)*D + d.
+ *     layout BASA_LAYOUT_BNHD: element (b,h,i,d) at ((b*n + i)*H + h)*D + d.
+ *     Memory tensors k_mem, v_mem are always [B, H, G, D] contiguous.
+ *   - A 2D grid is given as ndim = 2 with arrays (Hg, Wg); a 3D grid as
+ *     ndim = 3 with (T, Hg, Wg).  Window, shift and pool arrays have ndim
+ *     entries in the same axis order.
+ *   - dtype: BASA_BF16 (inputs and outputs bf16, fp32 accumulation and
+ *     softmax) or BASA_F32 (fp32 throughout).  All tensors of one call share
+ *     the dtype.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     Kernels run on the device current on the calling thread.  The library
+ *     enqueues work and returns; it never synchronises the stream.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory and holds no state between calls (reentrant).
+ *   - Errors: every call returns a status.  Arguments are validated before
+ *     anything is enqueued; on any error nothing is launched and no output
+ *     byte is written.  basa_last_error() gives a sentence naming the
+ *     argument at fault (per calling thread).  Faults inside a kernel show
+ *     up at the caller's next synchronisation, as for any HIP kernel.
+ */
+#ifndef BASA_H
+#define BASA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BASA_OK = 0,
+  BASA_ERR_INVALID_ARG = 1, /* null pointer, bad dim, non-dividing window/pool,
+                               n_mem mismatch, output overlapping an input   */
+  BASA_ERR_UNSUPPORTED = 2, /* dtype, head_dim or sizes outside what is built */
+  BASA_ERR_HIP = 3          /* the HIP runtime refused the launch            */
+};
+enum { BASA_F32 = 0, BASA_BF16 = 1 };
+enum { BASA_LAYOUT_BHND = 0, BASA_LAYOUT_BNHD = 1 };
+enum { BASA_SCHED_NONE = 0, BASA_SCHED_ALTERNATE = 1, BASA_SCHED_FOUR_PHASE = 2 };
+
+/* Largest window (tokens per window) basa_window_attn accepts. */
+#define BASA_MAX_WINDOW_TOKENS 4096
+
+/* Library ABI version (major*100 + minor). */
+int32_t basa_version(void);
+
+/* Text for a status code (static storage). */
+const char* basa_status_string(int32_t status);
+
+/* Sentence describing the last non-OK status returned on this thread. */
+const char* basa_last_error(void);
+
+/*
+ * Number of pooled memory tokens G = prod(grid[i] / pool[i]) [BASA-2, the
+ * global memory of pooled K/V; SFA, mean pooling].  Returns -1 when ndim is
+ * not 2 or 3, a pointer is NULL, a dim is not positive or a pool factor does
+ * not divide its grid dim.  Host only.
+ */
+int64_t basa_mem_tokens(int32_t ndim, const int32_t* grid, const int32_t* pool);
+
+/*
+ * Window shift for DiT block block_idx [BASA-1, "The BASA Method": the
+ * window partition shifts in a structured way from block to block]:
+ *   BASA_SCHED_NONE       zero shift;
+ *   BASA_SCHED_ALTERNATE  zero on even blocks, floor(window[i]/2) on odd;
+ *   BASA_SCHED_FOUR_PHASE phase = block_idx mod 2^ndim, axis i shifted by
+ *                         floor(window[i]/2) when bit i of phase is set
+ *                         (2D: (0,0), (w/2,0), (0,w/2), (w/2,w/2)).
+ * Writes ndim ints to shift_out (host).  Errors: INVALID_ARG for NULL,
+ * ndim not in {2,3}, block_idx < 0, window[i] <= 0, unknown schedule.
+ */
+int basa_shift_for_block(int32_t block_idx, int32_t schedule, int32_t ndim,
+                         const int32_t* window, int32_t* shift_out);
+
+/*
+ * Mean-pooled K/V memory [BASA-2, the global memory of pooled K/V; SFA,
+ * mean pooling]: k_mem[b,h,g,:] is the mean of k over pool cell g of the
+ * unshifted grid (cells in raster order of the pooled grid); the same for v.
+ * Accumulates in fp32 and stores in dtype (bf16 rounded to nearest even).
+ *   k, v          device, B x H x n x D in `layout`, n = prod(grid)
+ *   k_mem, v_mem  device, [B, H, G, D] contiguous, G = basa_mem_tokens()
+ *   batch, heads  >= 1;  head_dim in {64, 128}
+ *   ndim, grid, pool  host arrays of ndim entries; pool must divide grid
+ * Errors: INVALID_ARG (NULL, bad dims, pool not dividing the grid, an output
+ * overlapping an input or the other output), UNSUPPORTED (dtype, head_dim).
+ */
+int basa_pool_kv(const void* k, const void* v, void* k_mem, void* v_mem,
+                 int32_t batch, int32_t heads, int32_t head_dim,
+                 int32_t ndim, const int32_t* grid, const int32_t* pool,
+                 int32_t dtype, int32_t layout, void* stream);
+
+/*
+ * Shifted local window attention with optional pooled memory [BASA-1,
+ * "Summary" and "The BASA Method"; BASA-2 four-parts paragraph; SFA shared
+ * softmax].  For every token i of the grid
+ *   out[i] = softmax_j( scale * q[i].k[j] + bias_j ) v[j]
+ * over j in the window of i under the shifted partition, followed by the G
+ * memory tokens (bias_j = mem_bias for memory keys, 0 otherwise).  Token
+ * p = (t,y,x) lies in window ( ((t-st) mod T)/wt, ((y-sy) mod Hg)/wy,
+ * ((x-sx) mod Wg)/wx ) (integer division): the grid is cyclically rolled by
+ * -shift, cut into windows, attended, and rolled back.  Wrapped tokens are
+ * not masked.  No shifted copy is made: the roll is in the addressing.
+ *   q, k, v, out  device, B x H x n x D in `layout`; out must not overlap any
+ *                 input
+ *   k_mem, v_mem  device [B, H, n_mem, D] contiguous, or both NULL with
+ *                 n_mem = 0 for no memory.  n_mem is the number of memory
+ *                 rows (normally basa_mem_tokens() of the pool that made
+ *                 them); any n_mem in [1, 2^20] is accepted
+ *   window        divides grid on every axis; prod(window) <=
+ *                 BASA_MAX_WINDOW_TOKENS
+ *   shift         any integers; reduced modulo the window on each axis (a
+ *                 shift equal to the window is no shift)
+ *   scale         softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   mem_bias      added to every memory logit before the softmax (natural
+ *                 log units); 0 for the plain concatenation, ln(cell size)
+ *                 for the token-count corrected reading [SFA]
+ *   head_dim      {64, 128}
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype, head_dim, window too large).
+ */
+int basa_window_attn(const void* q, const void* k, const void* v,
+                     const void* k_mem, const void* v_mem, int64_t n_mem,
+                     void* out,
+                     int32_t batch, int32_t heads, int32_t head_dim,
+                     int32_t ndim, const int32_t* grid, const int32_t* window,
+                     const int32_t* shift, float scale, float mem_bias,
+                     int32_t dtype, int32_t layout, void* stream);
+
+/*
+ * Dense full attention out = softmax(scale * q k^T) v over all n_tokens keys
+ * per (batch, head) [BASA-2 complexity paragraph: the O(n^2) cost that window
+ * attention reduces to O(n*m)].  Built only to measure realised against
+ * theoretical speedup.  Arguments as for basa_window_attn; n_tokens >= 1.
+ */
+int basa_full_attn(const void* q, const void* k, const void* v, void* out,
+                   int32_t batch, int32_t heads, int64_t n_tokens,
+                   int32_t head_dim, float scale, int32_t dtype, int32_t layout,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASA_H */

@@ -1,0 +1,227 @@
+"""Python binding of the shifted-window sparse attention library (libbasa.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/basa.h``.  torch supplies
+device memory and the current stream.  Importing works without a GPU (the
+library loads and its host-only helpers run); compute calls need an MI355X.
+If ``libbasa.so`` is missing, import fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+__all__ = [
+    "BASA_OK", "BASA_ERR_INVALID_ARG", "BASA_ERR_UNSUPPORTED", "BASA_ERR_HIP",
+    "BASA_F32", "BASA_BF16", "BASA_LAYOUT_BHND", "BASA_LAYOUT_BNHD",
+    "SCHED_NONE", "SCHED_ALTERNATE", "SCHED_FOUR_PHASE", "BasaError", "lib",
+    "library_path", "version", "mem_tokens", "shift_for_block", "pool_kv",
+    "window_attn", "full_attn",
+]
+
+BASA_OK, BASA_ERR_INVALID_ARG, BASA_ERR_UNSUPPORTED, BASA_ERR_HIP = 0, 1, 2, 3
+BASA_F32, BASA_BF16 = 0, 1
+BASA_LAYOUT_BHND, BASA_LAYOUT_BNHD = 0, 1
+SCHED_NONE, SCHED_ALTERNATE, SCHED_FOUR_PHASE = 0, 1, 2
+MAX_WINDOW_TOKENS = 4096
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbasa.so")
+
+
+class BasaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (SONAME libamdhip64.so.7).  Importing
+    # torch first makes libbasa.so bind to that same runtime, so device
+    # pointers and streams from torch are valid in the library's calls; loading
+    # libbasa.so first would pull in a second runtime beside torch's.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is not built; run `python -m sparse_window_attention_amd._build`")
+    L = ctypes.CDLL(library_path)
+    i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "basa_version": (i32, []),
+        "basa_status_string": (ctypes.c_char_p, [i32]),
+        "basa_last_error": (ctypes.c_char_p, []),
+        "basa_mem_tokens": (i64, [i32, pi32, pi32]),
+        "basa_shift_for_block": (ctypes.c_int, [i32, i32, i32, pi32, pi32]),
+        "basa_pool_kv": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, pi32, pi32,
+                                        i32, i32, vp]),
+        "basa_window_attn": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32,
+                                            i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
+        "basa_full_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i64, i32, f32, i32,
+                                          i32, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _arr(vals: Sequence[int]):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _check(status: int) -> None:
+    if status != BASA_OK:
+        raise BasaError(status, f"{lib.basa_status_string(status).decode()}: "
+                                f"{lib.basa_last_error().decode()}")
+
+
+def version() -> int:
+    return int(lib.basa_version())
+
+
+def mem_tokens(grid: Sequence[int], pool: Sequence[int]) -> int:
+    g = lib.basa_mem_tokens(len(grid), _arr(grid), _arr(pool))
+    if g < 0:
+        raise BasaError(BASA_ERR_INVALID_ARG, lib.basa_last_error().decode())
+    return int(g)
+
+
+def shift_for_block(block: int, schedule: int, window: Sequence[int]) -> Tuple[int, ...]:
+    out = (ctypes.c_int32 * len(window))()
+    _check(lib.basa_shift_for_block(int(block), int(schedule), len(window), _arr(window), out))
+    return tuple(int(x) for x in out)
+
+
+# ------------------------------------------------------------ tensor calls
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BASA_BF16
+    if t.dtype == torch.float32:
+        return BASA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _layout_dims(t, layout: str):
+    if t.dim() != 4:
+        raise ValueError("tensors must be 4-D")
+    if layout == "bhnd":
+        B, H, n, D = t.shape
+        return B, H, n, D, BASA_LAYOUT_BHND
+    if layout == "bnhd":
+        B, n, H, D = t.shape
+        return B, H, n, D, BASA_LAYOUT_BNHD
+    raise ValueError("layout must be 'bhnd' or 'bnhd'")
+
+
+def _check_tensors(*ts):
+    t0 = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        if t.device != t0.device:
+            raise ValueError("tensors must share one device")
+        if t.dtype != t0.dtype:
+            raise ValueError("tensors must share one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def pool_kv(k, v, grid: Sequence[int], pool: Sequence[int], layout: str = "bhnd",
+            out: Optional[tuple] = None):
+    """Mean-pooled memory (k_mem, v_mem), each [B, H, G, D]."""
+    torch = _torch()
+    _check_tensors(k, v)
+    B, H, n, D, lay = _layout_dims(k, layout)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v shapes differ")
+    G = mem_tokens(grid, pool)
+    if out is None:
+        km = torch.empty((B, H, G, D), dtype=k.dtype, device=k.device)
+        vm = torch.empty_like(km)
+    else:
+        km, vm = out
+        _check_tensors(k, km, vm)
+        if tuple(km.shape) != (B, H, G, D) or tuple(vm.shape) != (B, H, G, D):
+            raise ValueError("memory outputs must be [B, H, G, D]")
+    if n != math.prod(grid):
+        raise ValueError("token count does not match the grid")
+    _check(lib.basa_pool_kv(k.data_ptr(), v.data_ptr(), km.data_ptr(), vm.data_ptr(), B, H, D,
+                            len(grid), _arr(grid), _arr(pool), _dtype_code(k), lay, _stream(k)))
+    return km, vm
+
+
+def window_attn(q, k, v, grid: Sequence[int], window: Sequence[int], shift: Sequence[int],
+                mem: Optional[tuple] = None, scale: Optional[float] = None,
+                mem_bias: float = 0.0, out=None, layout: str = "bhnd"):
+    """Shifted local window attention with optional pooled memory (k_mem, v_mem)."""
+    torch = _torch()
+    _check_tensors(q, k, v)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v shapes differ")
+    if n != math.prod(grid):
+        raise ValueError("token count does not match the grid")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out shape differs from q")
+    km_p = vm_p = None
+    G = 0
+    if mem is not None:
+        km, vm = mem
+        _check_tensors(q, km, vm)
+        if km.dim() != 4 or tuple(km.shape[:2]) != (B, H) or km.shape[3] != D \
+                or tuple(vm.shape) != tuple(km.shape):
+            raise ValueError("memory tensors must be [B, H, G, D]")
+        G = km.shape[2]
+        km_p, vm_p = km.data_ptr(), vm.data_ptr()
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_window_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, G,
+                                out.data_ptr(), B, H, D, len(grid), _arr(grid), _arr(window),
+                                _arr(shift), s, float(mem_bias), _dtype_code(q), lay,
+                                _stream(q)))
+    return out
+
+
+def full_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "bhnd"):
+    """Dense softmax(scale q k^T) v over all tokens of each (batch, head)."""
+    torch = _torch()
+    _check_tensors(q, k, v)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v shapes differ")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out)
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_full_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n,
+                              D, s, _dtype_code(q), lay, _stream(q)))
+    return out

@@ -1,0 +1,59 @@
+"""Builds libbasa.so (the HIP kernels and the C ABI) in place, for gfx950.
+
+Usage: python -m sparse_window_attention_amd._build
+"""
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libbasa.so")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # code object v5 loads in every ROCm 6/7 runtime, including the one torch bundles
+    "-mcode-object-version=5",
+    # no packed-fp32 instructions in any device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libbasa.so)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 feature: drop that warning
+    msg = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{msg}")
+    return msg
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        for msg in ex.map(_run, [[cc, *FLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]):
+            if verbose and msg:
+                print(msg)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o",
+          tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

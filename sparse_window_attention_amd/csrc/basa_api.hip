@@ -1,0 +1,304 @@
+// C ABI entry points: argument validation, geometry set-up and dispatch.
+// Every check runs before anything is enqueued, so a failing call launches
+// nothing and writes no output byte.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "basa_internal.h"
+
+namespace {
+
+thread_local char g_err[320] = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  snprintf(g_err, sizeof(g_err), "no error");
+  return BASA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Grid3 {
+  int32_t g[3];
+  int64_t n;
+};
+
+// Reads an ndim-entry host array into 3 entries (2D: leading 1 / fill).
+int read3(int32_t ndim, const int32_t* src, int32_t fill, int32_t out[3], const char* what) {
+  if (!src) return fail(BASA_ERR_INVALID_ARG, "%s is NULL", what);
+  if (ndim == 2) {
+    out[0] = fill;
+    out[1] = src[0];
+    out[2] = src[1];
+  } else {
+    out[0] = src[0];
+    out[1] = src[1];
+    out[2] = src[2];
+  }
+  return BASA_OK;
+}
+
+int check_grid(int32_t ndim, const int32_t* grid, int32_t g[3], int64_t* n) {
+  if (ndim != 2 && ndim != 3) return fail(BASA_ERR_INVALID_ARG, "ndim must be 2 or 3 (got %d)", ndim);
+  int rc = read3(ndim, grid, 1, g, "grid");
+  if (rc) return rc;
+  for (int i = 0; i < 3; ++i)
+    if (g[i] <= 0) return fail(BASA_ERR_INVALID_ARG, "grid dims must be positive");
+  *n = (int64_t)g[0] * g[1] * g[2];
+  return BASA_OK;
+}
+
+int check_divides(int32_t ndim, const int32_t* part, const int32_t g[3], int32_t out[3],
+                  const char* what) {
+  int rc = read3(ndim, part, 1, out, what);
+  if (rc) return rc;
+  for (int i = 0; i < 3; ++i) {
+    if (out[i] <= 0) return fail(BASA_ERR_INVALID_ARG, "%s dims must be positive", what);
+    if (g[i] % out[i]) return fail(BASA_ERR_INVALID_ARG, "%s does not divide the grid", what);
+  }
+  return BASA_OK;
+}
+
+int check_common(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, int32_t layout) {
+  if (batch <= 0 || heads <= 0) return fail(BASA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if ((int64_t)batch * heads > INT32_MAX / 2) return fail(BASA_ERR_UNSUPPORTED, "batch*heads too large");
+  if (dtype != BASA_BF16 && dtype != BASA_F32) return fail(BASA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(BASA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
+  if (layout != BASA_LAYOUT_BHND && layout != BASA_LAYOUT_BNHD)
+    return fail(BASA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  return BASA_OK;
+}
+
+// Strides (elements) of a B x H x n x D tensor in the given layout.
+void strides(int32_t layout, int32_t heads, int64_t n, int32_t D, int64_t* sb, int64_t* sh,
+             int64_t* stok) {
+  if (layout == BASA_LAYOUT_BHND) {
+    *sb = (int64_t)heads * n * D;
+    *sh = n * D;
+    *stok = D;
+  } else {
+    *sb = n * heads * D;
+    *sh = D;
+    *stok = (int64_t)heads * D;
+  }
+}
+
+float resolve_scale(float scale, int32_t D) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)D); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t basa_version(void) { return 100; }
+
+const char* basa_status_string(int32_t status) {
+  switch (status) {
+    case BASA_OK: return "BASA_OK";
+    case BASA_ERR_INVALID_ARG: return "BASA_ERR_INVALID_ARG: invalid argument";
+    case BASA_ERR_UNSUPPORTED: return "BASA_ERR_UNSUPPORTED: configuration not built";
+    case BASA_ERR_HIP: return "BASA_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* basa_last_error(void) { return g_err; }
+
+int64_t basa_mem_tokens(int32_t ndim, const int32_t* grid, const int32_t* pool) {
+  int32_t g[3], pl[3];
+  int64_t n;
+  if (check_grid(ndim, grid, g, &n)) return -1;
+  if (check_divides(ndim, pool, g, pl, "pool")) return -1;
+  ok();
+  return (int64_t)(g[0] / pl[0]) * (g[1] / pl[1]) * (g[2] / pl[2]);
+}
+
+int basa_shift_for_block(int32_t block_idx, int32_t schedule, int32_t ndim,
+                         const int32_t* window, int32_t* shift_out) {
+  if (ndim != 2 && ndim != 3) return fail(BASA_ERR_INVALID_ARG, "ndim must be 2 or 3 (got %d)", ndim);
+  if (!window || !shift_out) return fail(BASA_ERR_INVALID_ARG, "window or shift_out is NULL");
+  if (block_idx < 0) return fail(BASA_ERR_INVALID_ARG, "block index must be >= 0");
+  for (int i = 0; i < ndim; ++i)
+    if (window[i] <= 0) return fail(BASA_ERR_INVALID_ARG, "window dims must be positive");
+  int32_t s[3] = {0, 0, 0};
+  switch (schedule) {
+    case BASA_SCHED_NONE:
+      break;
+    case BASA_SCHED_ALTERNATE:
+      if (block_idx & 1)
+        for (int i = 0; i < ndim; ++i) s[i] = window[i] / 2;
+      break;
+    case BASA_SCHED_FOUR_PHASE: {
+      const int phase = block_idx % (1 << ndim);
+      for (int i = 0; i < ndim; ++i) s[i] = ((phase >> i) & 1) ? window[i] / 2 : 0;
+      break;
+    }
+    default:
+      return fail(BASA_ERR_INVALID_ARG, "unknown schedule %d", schedule);
+  }
+  for (int i = 0; i < ndim; ++i) shift_out[i] = s[i];
+  return ok();
+}
+
+int basa_pool_kv(const void* k, const void* v, void* k_mem, void* v_mem, int32_t batch,
+                 int32_t heads, int32_t head_dim, int32_t ndim, const int32_t* grid,
+                 const int32_t* pool, int32_t dtype, int32_t layout, void* stream) {
+  try {
+    if (!k || !v || !k_mem || !v_mem) return fail(BASA_ERR_INVALID_ARG, "k, v, k_mem and v_mem must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    int32_t g[3], pl[3];
+    int64_t n;
+    if ((rc = check_grid(ndim, grid, g, &n))) return rc;
+    if ((rc = check_divides(ndim, pool, g, pl, "pool"))) return rc;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_mem) || !aligned16(v_mem))
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n, head_dim, &sb, &sh, &stok);
+    if (n * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit token offsets");
+    const int64_t G = (int64_t)(g[0] / pl[0]) * (g[1] / pl[1]) * (g[2] / pl[2]);
+    const size_t es = dtype == BASA_BF16 ? 2 : 4;
+    const size_t in_bytes = (size_t)batch * heads * n * head_dim * es;
+    const size_t mem_bytes = (size_t)batch * heads * G * head_dim * es;
+    if (overlaps(k_mem, mem_bytes, k, in_bytes) || overlaps(k_mem, mem_bytes, v, in_bytes) ||
+        overlaps(v_mem, mem_bytes, k, in_bytes) || overlaps(v_mem, mem_bytes, v, in_bytes) ||
+        overlaps(k_mem, mem_bytes, v_mem, mem_bytes))
+      return fail(BASA_ERR_INVALID_ARG, "k_mem/v_mem overlap an input or each other");
+    basa::PoolParams p{};
+    p.k = k; p.v = v; p.kmem = k_mem; p.vmem = v_mem;
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.T = g[0]; p.Hg = g[1]; p.Wg = g[2];
+    p.pt = pl[0]; p.py = pl[1]; p.px = pl[2];
+    p.Gt = g[0] / pl[0]; p.Gy = g[1] / pl[1]; p.Gx = g[2] / pl[2];
+    p.G = (int32_t)G;
+    rc = basa::launch_pool(p, dtype, (hipStream_t)stream);
+    if (rc) return fail(rc, "pool launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_pool_kv");
+  }
+}
+
+int basa_window_attn(const void* q, const void* k, const void* v, const void* k_mem,
+                     const void* v_mem, int64_t n_mem, void* out, int32_t batch, int32_t heads,
+                     int32_t head_dim, int32_t ndim, const int32_t* grid, const int32_t* window,
+                     const int32_t* shift, float scale, float mem_bias, int32_t dtype,
+                     int32_t layout, void* stream) {
+  try {
+    if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    int32_t g[3], w[3], s[3];
+    int64_t n;
+    if ((rc = check_grid(ndim, grid, g, &n))) return rc;
+    if ((rc = check_divides(ndim, window, g, w, "window"))) return rc;
+    if ((rc = read3(ndim, shift, 0, s, "shift"))) return rc;
+    if ((k_mem == nullptr) != (v_mem == nullptr))
+      return fail(BASA_ERR_INVALID_ARG, "k_mem and v_mem must both be given or both be NULL");
+    if (k_mem && (n_mem < 1 || n_mem > (1 << 20)))
+      return fail(BASA_ERR_INVALID_ARG, "n_mem must be in [1, 2^20] with memory (got %lld)", (long long)n_mem);
+    if (!k_mem && n_mem != 0) return fail(BASA_ERR_INVALID_ARG, "n_mem must be 0 without memory");
+    if (isnan(scale) || isinf(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (isnan(mem_bias) || isinf(mem_bias)) return fail(BASA_ERR_INVALID_ARG, "mem_bias must be finite");
+    const int64_t m = (int64_t)w[0] * w[1] * w[2];
+    if (m > BASA_MAX_WINDOW_TOKENS)
+      return fail(BASA_ERR_UNSUPPORTED, "window of %lld tokens exceeds %d", (long long)m, BASA_MAX_WINDOW_TOKENS);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (k_mem && (!aligned16(k_mem) || !aligned16(v_mem))))
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n, head_dim, &sb, &sh, &stok);
+    if (n * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit token offsets");
+    const size_t es = dtype == BASA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)batch * heads * n * head_dim * es;
+    const size_t mb = k_mem ? (size_t)batch * heads * n_mem * head_dim * es : 0;
+    if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
+        overlaps(out, tb, k_mem, mb) || overlaps(out, tb, v_mem, mb))
+      return fail(BASA_ERR_INVALID_ARG, "out overlaps an input");
+
+    basa::AttnParams p{};
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.kmem = (const uint16_t*)k_mem; p.vmem = (const uint16_t*)v_mem; p.out = (uint16_t*)out;
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.m = (int32_t)m;
+    p.G = k_mem ? (int32_t)n_mem : 0;
+    p.nW = (int32_t)(n / m);
+    p.scale = resolve_scale(scale, head_dim);
+    p.c1 = p.scale * basa::kLog2e;
+    p.mem_bias = k_mem ? mem_bias : 0.0f;
+    p.mem_bias_raw = p.mem_bias / p.scale;
+    basa::Geometry& geo = p.geo;
+    geo.T = g[0]; geo.Hg = g[1]; geo.Wg = g[2];
+    geo.wt = w[0]; geo.wy = w[1]; geo.wx = w[2];
+    // any integer shift, reduced into [0, window)
+    geo.st = ((s[0] % w[0]) + w[0]) % w[0];
+    geo.sy = ((s[1] % w[1]) + w[1]) % w[1];
+    geo.sx = ((s[2] % w[2]) + w[2]) % w[2];
+    geo.nwy = g[1] / w[1];
+    geo.nwx = g[2] / w[2];
+    rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, false, (hipStream_t)stream)
+                            : basa::launch_attn_f32(p, false, (hipStream_t)stream);
+    if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
+    if (rc) return fail(rc, "window attention launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn");
+  }
+}
+
+int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                   int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
+                   int32_t layout, void* stream) {
+  try {
+    if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    if (n_tokens < 1) return fail(BASA_ERR_INVALID_ARG, "n_tokens must be >= 1");
+    if (isnan(scale) || isinf(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n_tokens, head_dim, &sb, &sh, &stok);
+    if (n_tokens * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "sequence too long for 32-bit token offsets");
+    const size_t es = dtype == BASA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)batch * heads * n_tokens * head_dim * es;
+    if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+      return fail(BASA_ERR_INVALID_ARG, "out overlaps an input");
+    basa::AttnParams p{};
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.kmem = nullptr; p.vmem = nullptr; p.out = (uint16_t*)out;
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.m = (int32_t)n_tokens;
+    p.G = 0;
+    p.nW = 1;
+    p.scale = resolve_scale(scale, head_dim);
+    p.c1 = p.scale * basa::kLog2e;
+    rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, true, (hipStream_t)stream)
+                            : basa::launch_attn_f32(p, true, (hipStream_t)stream);
+    if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
+    if (rc) return fail(rc, "full attention launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_full_attn");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Shared device-side types and helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace basa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Geometry of one call, in the kernels' terms.  Grids are 3D (T = 1 for
+// images).  Token offsets are element offsets inside one (batch, head) slice.
+struct Geometry {
+  int32_t T, Hg, Wg;        // grid
+  int32_t wt, wy, wx;       // window
+  int32_t st, sy, sx;       // shift, already reduced into [0, window)
+  int32_t nwy, nwx;         // windows along y and x
+};
+
+// Raster index of slot r of window j under the shifted partition: the grid
+// rolled by -shift, cut into windows, window j holds the tokens at
+// (j_axis*w_axis + r_axis + s_axis) mod grid_axis.
+__device__ __forceinline__ int32_t window_token(const Geometry& g, int32_t j, int32_t r) {
+  const int32_t rx = r % g.wx;
+  const int32_t rq = r / g.wx;
+  const int32_t ry = rq % g.wy;
+  const int32_t rt = rq / g.wy;
+  const int32_t jx = j % g.nwx;
+  const int32_t jq = j / g.nwx;
+  const int32_t jy = jq % g.nwy;
+  const int32_t jt = jq / g.nwy;
+  int32_t t = jt * g.wt + rt + g.st;
+  int32_t y = jy * g.wy + ry + g.sy;
+  int32_t x = jx * g.wx + rx + g.sx;
+  // the shift is below the window, itself no larger than the grid: at most
+  // one wrap per axis
+  t -= (t >= g.T) ? g.T : 0;
+  y -= (y >= g.Hg) ? g.Hg : 0;
+  x -= (x >= g.Wg) ? g.Wg : 0;
+  return (t * g.Hg + y) * g.Wg + x;
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+}  // namespace basa

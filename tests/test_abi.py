@@ -1,0 +1,165 @@
+"""C ABI checks that need no GPU.
+
+The library loads, exports every function include/basa.h declares, its
+host-only helpers give the right values, and every argument error is
+reported before anything is enqueued (the fake device pointers used here are
+never dereferenced: validation returns first).
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import sparse_window_attention_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "basa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+SZ = 1 << 30           # spacing between fake buffers (no false overlaps)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(basa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 8, names
+    lib = ctypes.CDLL(S.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, 1, 2, 3):
+        assert S.lib.basa_status_string(code).decode().startswith("BASA_")
+    assert S.lib.basa_status_string(99).decode() == "unknown status"
+    assert S.version() >= 100
+
+
+def test_shift_helper_matches_workload_text():
+    cases = json.load(open(os.path.join(GOLDEN, "shift_schedules.json")))["cases"]
+    for c in cases:
+        for b, want in enumerate(c["shifts"]):
+            assert list(S.shift_for_block(b, c["schedule"], c["window"])) == want, c["name"]
+    got = [S.shift_for_block(b, S.SCHED_FOUR_PHASE, (7, 10, 13)) for b in range(8)]
+    assert got == [(0, 0, 0), (3, 0, 0), (0, 5, 0), (3, 5, 0), (0, 0, 6), (3, 0, 6),
+                   (0, 5, 6), (3, 5, 6)]
+
+
+def test_shift_helper_errors():
+    for args in [(-1, 1, (2, 2)), (0, 7, (2, 2)), (0, 1, (0, 2))]:
+        with pytest.raises(S.BasaError) as e:
+            S.shift_for_block(*args)
+        assert e.value.status == S.BASA_ERR_INVALID_ARG
+    out = (ctypes.c_int32 * 4)()
+    assert S.lib.basa_shift_for_block(0, 1, 4, S._arr([2, 2, 2, 2]), out) == S.BASA_ERR_INVALID_ARG
+    assert S.lib.basa_shift_for_block(0, 1, 2, None, out) == S.BASA_ERR_INVALID_ARG
+
+
+def test_mem_tokens():
+    assert S.mem_tokens((64, 64), (4, 4)) == 256
+    assert S.mem_tokens((128, 128), (8, 8)) == 256
+    assert S.mem_tokens((21, 30, 52), (3, 5, 4)) == 546
+    assert S.mem_tokens((21, 30, 52), (1, 5, 4)) == 1638
+    assert S.mem_tokens((512, 512), (8, 8)) == 4096
+    for g, p in [((4, 6), (3, 3)), ((4, 6), (0, 3)), ((0, 6), (1, 3))]:
+        assert S.lib.basa_mem_tokens(2, S._arr(g), S._arr(p)) == -1
+    assert S.lib.basa_mem_tokens(4, S._arr((1, 2, 3, 4)), S._arr((1, 1, 1, 1))) == -1
+
+
+def _win(**kw):
+    a = dict(q=FAKE, k=FAKE + SZ, v=FAKE + 2 * SZ, km=None, vm=None, G=0, out=FAKE + 3 * SZ,
+             B=1, H=2, D=128, grid=(8, 8), window=(4, 4), shift=(0, 0), scale=-1.0, bias=0.0,
+             dtype=S.BASA_BF16, layout=S.BASA_LAYOUT_BHND)
+    a.update(kw)
+    nd = len(a["grid"])
+    return S.lib.basa_window_attn(
+        a["q"], a["k"], a["v"], a["km"], a["vm"], a["G"], a["out"], a["B"], a["H"], a["D"],
+        a.get("ndim", nd), S._arr(a["grid"]), S._arr(a["window"]), S._arr(a["shift"]),
+        a["scale"], a["bias"], a["dtype"], a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), S.BASA_ERR_INVALID_ARG),
+    (dict(out=None), S.BASA_ERR_INVALID_ARG),
+    (dict(ndim=4, grid=(8, 8, 8, 8), window=(4, 4, 4, 4), shift=(0, 0, 0, 0)), S.BASA_ERR_INVALID_ARG),
+    (dict(ndim=1, grid=(8,), window=(4,), shift=(0,)), S.BASA_ERR_INVALID_ARG),
+    (dict(grid=(8, 0)), S.BASA_ERR_INVALID_ARG),
+    (dict(window=(3, 4)), S.BASA_ERR_INVALID_ARG),
+    (dict(window=(0, 4)), S.BASA_ERR_INVALID_ARG),
+    (dict(km=FAKE + 4 * SZ), S.BASA_ERR_INVALID_ARG),               # k_mem without v_mem
+    (dict(km=FAKE + 4 * SZ, vm=FAKE + 5 * SZ, G=0), S.BASA_ERR_INVALID_ARG),
+    (dict(G=4), S.BASA_ERR_INVALID_ARG),                            # n_mem without memory
+    (dict(out=FAKE + 64), S.BASA_ERR_INVALID_ARG),                  # out overlaps q
+    (dict(km=FAKE + 4 * SZ, vm=FAKE + 3 * SZ + 256, G=4), S.BASA_ERR_INVALID_ARG),  # out overlaps v_mem
+    (dict(q=FAKE + 8), S.BASA_ERR_INVALID_ARG),                     # misaligned
+    (dict(B=0), S.BASA_ERR_INVALID_ARG),
+    (dict(layout=5), S.BASA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), S.BASA_ERR_INVALID_ARG),
+    (dict(bias=float("inf")), S.BASA_ERR_INVALID_ARG),
+    (dict(D=96), S.BASA_ERR_UNSUPPORTED),
+    (dict(dtype=7), S.BASA_ERR_UNSUPPORTED),
+    (dict(grid=(128, 128), window=(128, 64)), S.BASA_ERR_UNSUPPORTED),  # 8192-token window
+])
+def test_window_attn_validation(kw, code):
+    assert _win(**kw) == code
+    assert len(S.lib.basa_last_error().decode()) > 5
+
+
+def test_pool_validation():
+    f = S.lib.basa_pool_kv
+    args = lambda **kw: dict(dict(k=FAKE, v=FAKE + SZ, km=FAKE + 2 * SZ, vm=FAKE + 3 * SZ, B=1,
+                                  H=1, D=64, grid=(8, 8), pool=(4, 4), dtype=S.BASA_BF16,
+                                  layout=0), **kw)
+
+    def call(a):
+        return f(a["k"], a["v"], a["km"], a["vm"], a["B"], a["H"], a["D"], len(a["grid"]),
+                 S._arr(a["grid"]), S._arr(a["pool"]), a["dtype"], a["layout"], None)
+
+    assert call(args(k=None)) == S.BASA_ERR_INVALID_ARG
+    assert call(args(pool=(3, 4))) == S.BASA_ERR_INVALID_ARG
+    assert call(args(km=FAKE + 64)) == S.BASA_ERR_INVALID_ARG      # k_mem inside k
+    assert call(args(vm=FAKE + 2 * SZ + 16)) == S.BASA_ERR_INVALID_ARG  # k_mem/v_mem overlap
+    assert call(args(D=32)) == S.BASA_ERR_UNSUPPORTED
+    assert call(args(dtype=3)) == S.BASA_ERR_UNSUPPORTED
+
+
+def test_full_attn_validation():
+    f = S.lib.basa_full_attn
+    assert f(FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 3 * SZ, 1, 1, 0, 64, -1.0, 1, 0, None) \
+        == S.BASA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 16, 1, 1, 64, 64, -1.0, 1, 0, None) \
+        == S.BASA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 3 * SZ, 1, 1, 64, 80, -1.0, 1, 0, None) \
+        == S.BASA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 3 * SZ, 1, 1, 1 << 26, 128, -1.0, 1, 0,
+             None) == S.BASA_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        S.window_attn(x, x, x, (4, 4), (2, 2), (0, 0))
+    with pytest.raises(ValueError):
+        S.full_attn(x, x, x)
+
+
+def test_single_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch loaded, whatever the import order."""
+    import subprocess
+    import sys
+    code = ("import sparse_window_attention_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1"

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bars: bf16 max abs <= 2e-2 and mean abs <= 2e-3; fp32 max abs <= 1e-5, both
+against the float64 oracle on the exact input values.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import (assert_close, bhnd_to_bnhd, log, make_full_inputs, random_qkv,
+                      sample_windows, to_gpu, to_np)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+S = pytest.importorskip("sparse_window_attention_amd")
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------- tiny fp32
+@pytest.mark.parametrize("shift", [(4, 4), (0, 0), (-3, 9)])
+def test_tiny_f32(shift):
+    wl = W.TINY
+    log(f"tiny fp32 shift={shift}")
+    q, k, v = W.make_qkv(wl)
+    out = S.window_attn(to_gpu(q, "f32"), to_gpu(k, "f32"), to_gpu(v, "f32"), wl.grid, wl.window,
+                        shift, scale=1.0 / math.sqrt(64))
+    _sync()
+    ref = O.window_attention(q, k, v, wl.grid, wl.window, shift)
+    assert_close(to_np(out), ref, "f32", f"tiny shift {shift}")
+
+
+# ---------------------------------------------------- small multi-tile, ragged
+SMALL = [
+    # grid, window, pool, shift
+    ((24, 40), (12, 20), (4, 8), (5, 13)),
+    ((6, 10, 26), (3, 5, 13), (3, 5, 2), (1, 3, 7)),
+    ((6, 10, 26), (3, 5, 13), (1, 5, 13), (-1, -2, 20)),
+    ((16, 48), (16, 16), None, (8, 3)),
+    ((7, 9), (7, 9), (7, 9), (0, 0)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_geometries(case, D, dtype):
+    grid, window, pool, shift = SMALL[case]
+    n = int(np.prod(grid))
+    B, H = 2, 3
+    log(f"small case={case} D={D} dtype={dtype} grid={grid} window={window} pool={pool}")
+    q, k, v = random_qkv((B, H, n, D), dtype, seed=100 + case)
+    qg, kg, vg = (to_gpu(x, dtype) for x in (q, k, v))
+    mem = None
+    km = vm = None
+    if pool is not None:
+        mem = S.pool_kv(kg, vg, grid, pool)
+        km, vm = O.pool_mean(k, grid, pool), O.pool_mean(v, grid, pool)
+    out = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem)
+    _sync()
+    ref = O.window_attention(q, k, v, grid, window, shift, km, vm)
+    assert_close(to_np(out), ref, dtype, f"small {case} D{D} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bnhd_layout(dtype):
+    grid, window, pool, shift = SMALL[0]
+    n, B, H, D = int(np.prod(grid)), 2, 3, 128
+    log(f"bnhd layout {dtype}")
+    q, k, v = random_qkv((B, H, n, D), dtype, seed=7)
+    ref = O.window_attention(q, k, v, grid, window, shift, O.pool_mean(k, grid, pool),
+                             O.pool_mean(v, grid, pool))
+    qg, kg, vg = (to_gpu(bhnd_to_bnhd(x), dtype) for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool, layout="bnhd")
+    out = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem, layout="bnhd")
+    _sync()
+    got = np.transpose(to_np(out), (0, 2, 1, 3))
+    assert_close(got, ref, dtype, f"bnhd {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_token_count_corrected_memory(dtype):
+    grid, window, pool, shift = (16, 32), (8, 8), (4, 4), (3, 5)
+    n, B, H, D = 512, 1, 2, 64
+    log(f"memory logit bias {dtype}")
+    q, k, v = random_qkv((B, H, n, D), dtype, seed=8)
+    bias = math.log(16.0)
+    qg, kg, vg = (to_gpu(x, dtype) for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool)
+    out = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem, mem_bias=bias)
+    _sync()
+    ref = O.window_attention(q, k, v, grid, window, shift, O.pool_mean(k, grid, pool),
+                             O.pool_mean(v, grid, pool), mem_logit_bias=bias)
+    assert_close(to_np(out), ref, dtype, f"mem bias {dtype}")
+
+
+# ------------------------------------------------------------------ pooling
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+def test_pool_kv(dtype, layout):
+    grid, pool = (6, 20, 24), (3, 5, 4)
+    n, B, H, D = 2880, 2, 2, 128
+    log(f"pool {dtype} {layout}")
+    _, k, v = random_qkv((B, H, n, D), dtype, seed=9)
+    conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)
+    km, vm = S.pool_kv(to_gpu(conv(k), dtype), to_gpu(conv(v), dtype), grid, pool, layout=layout)
+    _sync()
+    for got, x in ((km, k), (vm, v)):
+        ref = O.pool_mean(x, grid, pool)
+        err = np.abs(to_np(got) - ref)
+        # bf16: one rounding of the mean (half an ulp, relative 2^-9) plus fp32 sums
+        tol = (np.abs(ref) * 2.0 ** -8 + 1e-6) if dtype == "bf16" else (np.abs(ref) * 1e-6 + 1e-6)
+        assert np.all(err <= tol), float(err.max())
+
+
+# ------------------------------------------------------------ full-size configs
+@pytest.mark.parametrize("block", [0, 1])
+def test_flux1024_full(block):
+    wl = W.FLUX1024
+    shift = S.shift_for_block(block, wl.schedule, wl.window)
+    log(f"flux1024 block={block} shift={shift}")
+    q, k, v = W.make_qkv(wl)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, wl.grid, wl.pool)
+    out = S.window_attn(qg, kg, vg, wl.grid, wl.window, shift, mem=mem)
+    _sync()
+    ref = O.window_attention(q, k, v, wl.grid, wl.window, shift, O.pool_mean(k, wl.grid, wl.pool),
+                             O.pool_mean(v, wl.grid, wl.pool))
+    assert_close(to_np(out), ref, "bf16", f"flux1024 block {block}")
+
+
+def _sampled_check(wl, shift, heads, windows, variant=0):
+    gpu, exact = make_full_inputs(wl, heads, variant)
+    qg, kg, vg = gpu
+    mem = None
+    if wl.pool is not None:
+        mem = S.pool_kv(kg, vg, wl.grid, wl.pool)
+    out = S.window_attn(qg, kg, vg, wl.grid, wl.window, shift, mem=mem)
+    _sync()
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+    for h in heads:
+        q, k, v = exact[h]
+        km = vm = None
+        if wl.pool is not None:
+            km = O.pool_mean(k[None, None], wl.grid, wl.pool)[0, 0]
+            vm = O.pool_mean(v[None, None], wl.grid, wl.pool)[0, 0]
+        idx, ref = O.window_attention_head(q, k, v, wl.grid, wl.window, shift, km, vm,
+                                           windows=windows)
+        got = to_np(out[0, h][torch.from_numpy(idx.reshape(-1)).to(out.device)])
+        assert_close(got.reshape(ref.shape), ref, "bf16",
+                     f"{wl.name} head {h} shift {shift} windows {windows}")
+
+
+@pytest.mark.parametrize("wl", [W.FLUX2048_W16, W.FLUX2048_W32], ids=lambda w: w.name)
+def test_flux2048_sampled(wl):
+    for block in range(4):
+        shift = S.shift_for_block(block, wl.schedule, wl.window)
+        log(f"{wl.name} block={block} shift={shift}")
+        _sampled_check(wl, shift, heads=[0, 13, 23], windows=sample_windows(wl.n_windows))
+
+
+@pytest.mark.parametrize("wl", [W.WAN, W.WAN_G1638], ids=lambda w: w.name)
+def test_wan_sampled(wl):
+    for block in range(2):
+        shift = S.shift_for_block(block, wl.schedule, wl.window)
+        log(f"{wl.name} block={block} shift={shift}")
+        _sampled_check(wl, shift, heads=[0, 21, 39], windows=sample_windows(wl.n_windows))
+
+
+def test_ultra_sampled():
+    wl = W.ULTRA
+    shift = S.shift_for_block(3, wl.schedule, wl.window)
+    log(f"{wl.name} shift={shift}")
+    _sampled_check(wl, shift, heads=[5, 19], windows=sample_windows(wl.n_windows, 3))
+
+
+# ------------------------------------------------------------- dense kernel
+@pytest.mark.parametrize("dtype,n,D", [("bf16", 4096, 128), ("bf16", 1000, 128),
+                                       ("bf16", 777, 64), ("f32", 300, 64), ("f32", 520, 128)])
+def test_full_attn(dtype, n, D):
+    B, H = 1, 3
+    log(f"full attention {dtype} n={n} D={D}")
+    q, k, v = random_qkv((B, H, n, D), dtype, seed=n + D)
+    out = S.full_attn(to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype))
+    _sync()
+    rows = np.unique(np.linspace(0, n - 1, min(n, 300)).astype(np.int64))
+    ref = O.full_attention(q, k, v, rows=rows)
+    assert_close(to_np(out)[:, :, rows], ref, dtype, f"full {dtype} n{n} D{D}")
+
+
+def test_window_equal_grid_matches_full_kernel():
+    grid = (32, 32)
+    log("window = grid vs dense kernel")
+    q, k, v = random_qkv((1, 2, 1024, 128), "bf16", seed=11)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    a = S.window_attn(qg, kg, vg, grid, grid, (0, 0))
+    b = S.full_attn(qg, kg, vg)
+    _sync()
+    assert torch.equal(a, b)
+    assert_close(to_np(a), O.full_attention(q, k, v), "bf16", "window=grid")
+
+
+# ------------------------------------------------------- sentinels and guards
+def test_output_fully_written_and_guards_intact():
+    grid, window, pool, shift = SMALL[1]
+    n, B, H, D = int(np.prod(grid)), 2, 3, 128
+    log("NaN sentinel + guard canaries")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=12)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool)
+    numel = B * H * n * D
+    pad = 4096
+    buf = torch.full((numel + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=qg.device)
+    buf[:pad] = 7.0
+    buf[-pad:] = -7.0
+    out = buf[pad:pad + numel].view(B, H, n, D)
+    S.window_attn(qg, kg, vg, grid, window, shift, mem=mem, out=out)
+    _sync()
+    assert bool(torch.isfinite(out).all())
+    assert bool((buf[:pad] == 7.0).all()) and bool((buf[-pad:] == -7.0).all())
+
+
+def test_deterministic_and_shift_period():
+    wl = W.FLUX1024
+    log("determinism and shift period")
+    q, k, v = random_qkv((1, 4, wl.n_tokens, 128), "bf16", seed=13)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, wl.grid, wl.pool)
+    a = S.window_attn(qg, kg, vg, wl.grid, wl.window, (8, 8), mem=mem)
+    b = S.window_attn(qg, kg, vg, wl.grid, wl.window, (8, 8), mem=mem)
+    c = S.window_attn(qg, kg, vg, wl.grid, wl.window, (8 + 16, 8 - 32), mem=mem)
+    z0 = S.window_attn(qg, kg, vg, wl.grid, wl.window, (0, 0), mem=mem)
+    zw = S.window_attn(qg, kg, vg, wl.grid, wl.window, (16, 16), mem=mem)
+    _sync()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+    assert torch.equal(z0, zw)
+    assert not torch.equal(a, z0)
+
+
+def test_binding_errors_before_launch():
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(S.BasaError):
+        S.window_attn(x, x, x.clone(), (8, 8), (3, 8), (0, 0))
+    with pytest.raises(S.BasaError):
+        S.window_attn(x, x, x, (8, 8), (4, 4), (0, 0), out=x)    # out aliases q
