@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Throughput of the shifted-window attention hot path on one MI355X.
+
+A step is one DiT block's attention on the FLUX-like 2048px image shape
+(128x128 = 16384 tokens, 24 heads, head dim 128, bf16): the block's window
+shift from the 4-phase schedule, mean pooling of K/V into 256 memory tokens
+(8x8 cells), and shifted-window attention over [window keys; memory keys].
+Steps cycle through the 4 schedule phases and through several input sets
+(> 1 GB in total, so no step finds its inputs in the 256 MB last-level
+cache); inputs are resident in HBM before timing starts.
+
+Printed: one JSON line.  ``value`` is the window-attention algorithmic
+TFLOP/s per step (4*B*H*n*(m+G)*D flops over the step time, pool included).
+Both windows (16x16 and 32x32) are measured; ``--window`` picks the headline.
+The dense kernel of the same library is timed at the same shape for the
+realised-versus-theoretical speedup, and the CPU oracle is timed on a
+bounded sample (``cpu_baseline``).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (vendor figure)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (vendor figure)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_attn_traffic.json")
+KERNEL_SOURCES = ["sparse_window_attention_amd/csrc/attn_bf16.hip",
+                  "sparse_window_attention_amd/csrc/basa_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--window", type=int, default=16, choices=(16, 32))
+    ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
+    ap.add_argument("--dense-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=("window", "all"), default="all",
+                    help="'window': time only the headline steps (for profilers)")
+    return ap.parse_args()
+
+
+# Work model of one call (algorithmic: the work the method must do, not the
+# padding or L2 re-reads an implementation adds).
+def window_flops(B, H, n, m, G, D):
+    return 4 * B * H * n * (m + G) * D
+
+
+def dense_flops(B, H, n, D):
+    return 4 * B * H * n * n * D
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def make_sets(wl, nsets, dev):
+    import torch
+    import workloads as W
+    sets = []
+    for s in range(nsets):
+        q, k, v = W.make_qkv(wl, variant=s)
+        sets.append(tuple(torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v)))
+    return sets
+
+
+def time_steps(S, wl, sets, steps, warmup, stream, with_mem=True):
+    """Runs warmup + timed steps; returns (ms/step, pool ms list, attn ms list)."""
+    import torch
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    G = wl.mem_tokens
+    dev = sets[0][0].device
+    outs = [torch.empty_like(s[0]) for s in sets]
+    mems = [(torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev)) for _ in sets]
+
+    def step(i, ev=None):
+        si = i % len(sets)
+        q, k, v = sets[si]
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        if ev is not None:
+            ev[0].record(stream)
+        mem = None
+        if with_mem:
+            mem = S.pool_kv(k, v, wl.grid, wl.pool, out=mems[si])
+        if ev is not None:
+            ev[1].record(stream)
+        S.window_attn(q, k, v, wl.grid, wl.window, shift, mem=mem, out=outs[si])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    pool = [e[0].elapsed_time(e[1]) for e in evs]
+    attn = [e[1].elapsed_time(e[2]) for e in evs]
+    return total / steps, pool, attn
+
+
+def time_dense(S, sets, reps, stream):
+    import torch
+    q, k, v = sets[0]
+    out = torch.empty_like(q)
+    S.full_attn(q, k, v, out=out)
+    torch.cuda.synchronize()
+    ts = []
+    for r in range(reps):
+        q, k, v = sets[r % len(sets)]
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        S.full_attn(q, k, v, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return ts
+
+
+def median(x):
+    x = sorted(x)
+    return x[len(x) // 2] if len(x) % 2 else 0.5 * (x[len(x) // 2 - 1] + x[len(x) // 2])
+
+
+def pct(x, p):
+    x = sorted(x)
+    return x[min(len(x) - 1, max(0, int(round(p / 100.0 * (len(x) - 1)))))]
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, untuned, on a bounded sample of the headline workload:
+    whole heads (every window, pooled memory) until ~target_s of CPU time."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cache = {}
+    calls, heads_done, flops, t_total = 0, 0, 0, 0.0
+    # whole heads, cycling through the schedule phases, until ~target_s
+    while t_total < target_s and heads_done < 4 * wl.heads:
+        h, block = heads_done % wl.heads, heads_done // wl.heads
+        if h not in cache:
+            cache[h] = tuple(W.head_values(wl, t, h) for t in range(3))
+        q, k, v = cache[h]
+        shift = O.shift_for_block(block, wl.schedule, wl.window)
+        t0 = time.perf_counter()
+        km = O.pool_mean(k[None, None], wl.grid, wl.pool)[0, 0]
+        vm = O.pool_mean(v[None, None], wl.grid, wl.pool)[0, 0]
+        O.window_attention_head(q, k, v, wl.grid, wl.window, shift, km, vm)
+        t_total += time.perf_counter() - t0
+        heads_done += 1
+        flops += O.window_flops(1, 1, wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim)
+    tflops = flops / t_total / 1e12
+    ms_per_call = t_total / heads_done * wl.heads * 1e3
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads_done} head-blocks (head x schedule phase, {wl.heads} heads per "
+                      f"call) of {wl.name}, all {wl.n_windows} windows each, pool included, "
+                      f"fp64 numpy; {t_total:.1f} s of oracle time",
+            "ms_per_call_extrapolated": ms_per_call,
+            "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+
+
+def measure_window(S, wl, args, stream, dev, with_dense=True):
+    n, m, G, D, H, B = (wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.heads,
+                       wl.batch)
+    sets = make_sets(wl, args.sets, dev)
+    ms_step, pool, attn = time_steps(S, wl, sets, args.steps, args.warmup, stream, True)
+    flops = window_flops(B, H, n, m, G, D)
+    flops_nomem = window_flops(B, H, n, m, 0, D)
+    attn_bytes = 4 * B * H * n * D * 2 + 2 * B * H * G * D * 2
+    pool_bytes = 2 * B * H * n * D * 2 + 2 * B * H * G * D * 2
+    attn_ms = sum(attn) / len(attn)
+    pool_ms = sum(pool) / len(pool)
+    r = {
+        "workload": wl.name, "n": n, "m": m, "G": G,
+        "ms_per_step": ms_step,
+        "tflops_per_step": flops / (ms_step * 1e-3) / 1e12,
+        "window_attn_ms": {"mean": attn_ms, "median": median(attn), "p10": pct(attn, 10),
+                           "p90": pct(attn, 90)},
+        "pool_kv_ms": {"mean": pool_ms, "median": median(pool)},
+        "window_attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
+        "window_attn_mfma_frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "window_attn_gbs": attn_bytes / (attn_ms * 1e-3) / 1e9,
+        "pool_kv_gbs": pool_bytes / (pool_ms * 1e-3) / 1e9,
+        "flops_per_call": flops, "attn_bytes_per_call": attn_bytes,
+        "pool_bytes_per_call": pool_bytes,
+    }
+    # memory off: the literal n/m comparison
+    _, _, attn0 = time_steps(S, wl, sets, max(10, args.steps // 2), 3, stream, False)
+    attn0_ms = sum(attn0) / len(attn0)
+    r["window_attn_nomem_ms"] = attn0_ms
+    r["window_attn_nomem_tflops"] = flops_nomem / (attn0_ms * 1e-3) / 1e12
+    if with_dense:
+        dense = time_dense(S, sets, args.dense_reps, stream)
+        dense_ms = median(dense)
+        dflops = dense_flops(B, H, n, D)
+        r["dense_ms"] = dense_ms
+        r["dense_tflops"] = dflops / (dense_ms * 1e-3) / 1e12
+        r["dense_mfma_frac"] = r["dense_tflops"] / PEAK_BF16_TFLOPS
+        th_nomem = n / m
+        th_mem = n / (m + G)
+        r["speedup"] = {
+            "theoretical_n_over_m": th_nomem,
+            "realised_nomem": dense_ms / attn0_ms,
+            "realised_over_theoretical_nomem": dense_ms / attn0_ms / th_nomem,
+            "theoretical_n_over_m_plus_G": th_mem,
+            "realised_mem": dense_ms / attn_ms,
+            "realised_over_theoretical_mem": dense_ms / attn_ms / th_mem,
+            "realised_mem_incl_pool": dense_ms / (attn_ms + pool_ms),
+        }
+    del sets
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import sparse_window_attention_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    head = W.FLUX2048_W16 if args.window == 16 else W.FLUX2048_W32
+    other = W.FLUX2048_W32 if args.window == 16 else W.FLUX2048_W16
+    print(f"[bench] headline {head.name}: {args.warmup} warmup + {args.steps} timed steps",
+          file=sys.stderr, flush=True)
+    if args.only == "window":
+        sets = make_sets(head, args.sets, dev)
+        ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)
+        print(json.dumps({"ms_per_step": ms, "attn_ms": sum(attn) / len(attn),
+                          "pool_ms": sum(pool) / len(pool)}))
+        return
+    res = measure_window(S, head, args, stream, dev)
+    print(f"[bench] {head.name}: attn {res['window_attn_ms']['mean']*1e3:.1f} us "
+          f"({res['window_attn_tflops']:.0f} TFLOP/s), pool {res['pool_kv_ms']['mean']*1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    res_o = measure_window(S, other, args, stream, dev)
+    print(f"[bench] {other.name}: attn {res_o['window_attn_ms']['mean']*1e3:.1f} us "
+          f"({res_o['window_attn_tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+
+    # roofline of the dominant kernel (window attention) on the headline workload
+    flops = res["flops_per_call"]
+    byts = res["attn_bytes_per_call"]
+    t = res["window_attn_ms"]["mean"] * 1e-3
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / byts >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "attn_bf16_kernel<128,false>"
+    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = byts
+    roof["mfma_frac"] = res["window_attn_mfma_frac"]
+    roof["kernel_source_hash"] = kernel_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_source_hash") == roof["kernel_source_hash"] and \
+                    tr.get("workload") == head.name:
+                roof["traffic"] = tr["hbm_bytes_per_launch"]
+        except Exception:
+            pass
+
+    line = {
+        "metric": "ms/attn call + effective TFLOP/s (MFMA util) at FLUX-2048 shape; "
+                  "realised/theory speedup",
+        "value": res["tflops_per_step"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": head.name, "global_batch": head.batch, "seq_len": head.n_tokens,
+                   "heads": head.heads, "head_dim": head.head_dim, "grid": list(head.grid),
+                   "window": list(head.window), "pool": list(head.pool),
+                   "mem_tokens": head.mem_tokens, "schedule": "four-phase",
+                   "input_sets_rotated": args.sets, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "ms_per_attn_call": res["window_attn_ms"]["mean"],
+        "windows": {f"{res['m']}": res, f"{res_o['m']}": res_o},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
