@@ -46,8 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=("window", "all"), default="all",
-                    help="'window': time only the headline steps (for profilers)")
+    ap.add_argument("--only", choices=("window", "dense", "all"), default="all",
+                    help="'window': only the headline steps; 'dense': only the dense kernel "
+                         "at the same shape (for profilers)")
     return ap.parse_args()
 
 
@@ -257,6 +258,11 @@ def main():
     other = W.FLUX2048_W32 if args.window == 16 else W.FLUX2048_W16
     print(f"[bench] headline {head.name}: {args.warmup} warmup + {args.steps} timed steps",
           file=sys.stderr, flush=True)
+    if args.only == "dense":
+        sets = make_sets(head, 1, dev)
+        ts = time_dense(S, sets, args.steps, stream)
+        print(json.dumps({"dense_ms": median(ts)}))
+        return
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
         ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)

@@ -27,7 +27,9 @@ BASA_LAYOUT_BHND, BASA_LAYOUT_BNHD = 0, 1
 SCHED_NONE, SCHED_ALTERNATE, SCHED_FOUR_PHASE = 0, 1, 2
 MAX_WINDOW_TOKENS = 4096
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbasa.so")
+# BASA_LIBRARY may point at another build of the same library (tuning runs).
+library_path = os.environ.get("BASA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libbasa.so")
 
 
 class BasaError(RuntimeError):

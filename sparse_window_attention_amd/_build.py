@@ -10,15 +10,20 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libbasa.so")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # code object v5 loads in every ROCm 6/7 runtime, including the one torch bundles
     "-mcode-object-version=5",
+    # no NaN reaches these kernels (inputs are finite, masks use -inf): lets
+    # max/min skip NaN canonicalisation
+    "-fno-honor-nans",
     # no packed-fp32 instructions in any device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}",
 ]
 
 
@@ -38,21 +43,25 @@ def _run(cmd):
     return msg
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compiles every csrc/*.hip and links ``out``; ``defines`` are extra -D
+    macros (kernel tuning knobs, default values otherwise)."""
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    dflags = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        for msg in ex.map(_run, [[cc, *FLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]):
+        for msg in ex.map(_run, [[cc, *FLAGS, *dflags, "-c", s, "-o", o]
+                                 for s, o in zip(srcs, objs)]):
             if verbose and msg:
                 print(msg)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o",
           tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/basa.h"
+#include "basa.h"
 #include "basa_common.h"
 
 namespace basa {
