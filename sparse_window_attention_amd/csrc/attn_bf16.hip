@@ -1,16 +1,17 @@
 // bf16 window / full attention on gfx950 matrix cores.
 //
-// One workgroup computes kQT query rows of one window of one (batch, head).
-// The window's keys and the pooled memory keys form one virtual key sequence
+// A work unit is kQT query rows of one window of one (batch, head).  The
+// window's keys and the pooled memory keys form one virtual key sequence
 // [window keys; memory keys] of length L = m + G, streamed through LDS in
-// tiles of kKT keys.  Per tile and wave:
+// tiles of kKT keys.  Each wave owns QB blocks of 32 query rows; per tile:
 //   S^T = K Q^T        (32x32x16 bf16 MFMA, keys x queries, fp32 accumulate)
 //   online softmax     (fp32, base 2; the row max needs one lane swap since a
 //                       lane holds 16 keys of one query)
 //   O^T += V^T P^T     (32x32x16 bf16 MFMA, P rounded to bf16)
 // Computing S transposed puts every query in one lane pair, so the softmax
 // reductions stay in registers, and the fp32 scores already sit in the
-// operand layout the P V product needs (no shuffles).
+// operand layout the P V product needs (no shuffles).  Every K or V operand
+// read from LDS feeds the QB query blocks of the wave.
 //
 // The loop is software-pipelined inside each wave: while the exponentials of
 // tile t are computed on the vector ALU, the matrix core already runs
@@ -18,11 +19,11 @@
 // t.  K runs one tile ahead of V through two LDS buffers each.
 //
 // The cyclic shift and the window gather are address arithmetic: a table of
-// the window's raster offsets is built in LDS once per workgroup and every
-// Q/K/V/O row is addressed through it (BASA forum summary, "The BASA
-// Method": shift, partition, attend, shift back -- here without any copy).
-// Memory keys (BASA discussion reply, the four parts of the method: a global
-// memory of pooled K/V) are plain rows of the [B,H,G,D] memory tensors.
+// the window's raster offsets is built in LDS per unit and every Q/K/V/O row
+// is addressed through it (BASA forum summary, "The BASA Method": shift,
+// partition, attend, shift back -- here without any copy).  Memory keys
+// (BASA discussion reply, the four parts of the method: a global memory of
+// pooled K/V) are plain rows of the [B,H,G,D] memory tensors.
 #include <type_traits>
 
 #include "basa_common.h"
@@ -32,26 +33,30 @@ namespace basa {
 
 namespace {
 
-constexpr int kQPW = 32;              // query rows per wave
-constexpr int kKT = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
 
-template <int D, int NW>
+template <int D, int NW, int QB, int KT>
 struct Tiles {
+  static constexpr int kKT = KT;                  // keys per tile
+  static constexpr int KB = KT / 32;              // 32-key blocks per tile
   static constexpr int kThreads = NW * 64;
-  static constexpr int kQT = NW * kQPW;           // query rows per workgroup
+  static constexpr int kQPW = 32 * QB;            // query rows per wave
+  static constexpr int kQT = NW * kQPW;           // query rows per unit
   static constexpr int KS = D + 8;    // K tile row stride (bf16), 16B aligned, skewed banks
   static constexpr int VS = kKT + 8;  // transposed V tile row stride (bf16)
   static constexpr int kBytes = kKT * KS * 2;
   static constexpr int vBytes = D * VS * 2;
-  static constexpr int ldsBytes = 2 * kBytes + 2 * vBytes;
+  static constexpr int tileBytes = 2 * kBytes + 2 * vBytes;
   static constexpr int CPR = D / 8;               // 16B chunks per row
   static constexpr int RPP = kThreads / CPR;      // K rows per load pass
   static constexpr int KPASS = kKT / RPP;         // K load passes per tile
   static constexpr int KPT = kKT * D / (kThreads * 8);  // V keys per thread
+  static_assert(KPASS >= 1 && KPASS * RPP == kKT, "K tile must split evenly over the threads");
+  static_assert(KPT >= 1 && KPT <= 4 && KPT * kThreads * 8 == kKT * D,
+                "V tile must split evenly over the threads");
 };
 
-// Slot of key `key` (0..kKT-1) in the transposed V tile: within each group of
+// Slot of key `key` (0..KT-1) in the transposed V tile: within each group of
 // 16 keys, the order matches how the S^T accumulator registers map onto the
 // k index of the P V product's operand.
 __device__ __forceinline__ int vslot(int key) {
@@ -62,105 +67,158 @@ __device__ __forceinline__ int vslot(int key) {
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-template <int D, bool FULL, int NW>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_bf16_kernel(AttnParams p) {
-  using TL = Tiles<D, NW>;
-  constexpr int kThreads = TL::kThreads;
-  constexpr int kQT = TL::kQT;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int32_t* sOff = reinterpret_cast<int32_t*>(smem + TL::ldsBytes);
-  auto sK = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + buf * TL::kBytes); };
-  auto sV = [&](int buf) __attribute__((always_inline)) {
-    return reinterpret_cast<uint16_t*>(smem + 2 * TL::kBytes + buf * TL::vBytes);
-  };
+// One work unit: element offset of its (batch, head) slice in Q/K/V/O, its
+// (batch, head) index, window and query tile.
+struct Unit {
+  int64_t base;
+  int bh;
+  int win;
+  int qt;
+};
 
-  // ---- work unit (XCD-aware: consecutive units run on one XCD's L2)
-  const int xcd = blockIdx.x & 7;
-  const int kidx = blockIdx.x >> 3;
-  const int unit = xcd * p.units_per_xcd + kidx;
-  if (kidx >= p.units_per_xcd || unit >= p.units) return;
-  const int qt = unit % p.nQT;
+__device__ __forceinline__ Unit decode_unit(const AttnParams& p, int unit) {
+  Unit u;
+  u.qt = unit % p.nQT;
   const int rest = unit / p.nQT;
-  const int win = rest % p.nW;
-  const int bh = rest / p.nW;
-  const int b = bh / p.heads, h = bh - b * p.heads;
-  const int64_t base = (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
-  const uint16_t* __restrict__ gq = p.q + base;
-  const uint16_t* __restrict__ gk = p.k + base;
-  const uint16_t* __restrict__ gv = p.v + base;
-  uint16_t* __restrict__ go = p.out + base;
-  const uint16_t* __restrict__ gkm = p.kmem + (int64_t)bh * p.G * D;
-  const uint16_t* __restrict__ gvm = p.vmem + (int64_t)bh * p.G * D;
+  u.win = rest % p.nW;
+  u.bh = rest / p.nW;
+  const int b = u.bh / p.heads, h = u.bh - b * p.heads;
+  u.base = (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
+  return u;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;
-  const int m = p.m;
-  const int L = m + p.G;
-  const int stok = p.stride_tok;
+// Everything one wave keeps for the attention of its query rows, and the
+// tile staging of the whole workgroup.
+template <int D, bool FULL, int NW, int QB, int KT>
+struct Core {
+  using TL = Tiles<D, NW, QB, KT>;
+  static constexpr int kKT = KT;
+  static constexpr int KB = TL::KB;
+  static constexpr int QS = D / 16;   // MFMA k-steps over the head dim
+  static constexpr int DB = D / 32;   // 32-row blocks of O^T
+  using Scores = f32x16[QB][KB];      // S^T of one tile: [query block][32-key block]
+  using Probs = u32x4[QB][2 * KB];    // bf16 P^T operands: [query block][16-key slice]
 
-  if (!FULL) {
-    for (int r = tid; r < m; r += kThreads) sOff[r] = window_token(p.geo, win, r) * stok;
-    __syncthreads();
+  const AttnParams& p;
+  unsigned char* smem;
+  int tid, wave, l32, hf;
+  int m, L, stok, tmask, nkt;
+  float c1, bias;
+  int kc, kr0, va, vc;                // tile loader geometry
+  u32x4 qreg[QB][QS];                 // Q rows (B operand of K Q^T)
+  u32x4 kreg[TL::KPASS];              // staged K rows
+  u32x4 vreg[TL::KPT];                // staged V rows
+  f32x16 acc[QB][DB];                 // O^T accumulators
+  float m_used[QB];                   // lagging max (log2 units)
+  float l0[QB], l1[QB];               // this lane's row sum halves
+
+  __device__ __forceinline__ Core(const AttnParams& pp, unsigned char* sm) : p(pp), smem(sm) {
+    tid = threadIdx.x;
+    const int lane = tid & 63;
+    wave = tid >> 6;
+    l32 = lane & 31;
+    hf = lane >> 5;
+    m = p.m;
+    L = m + p.G;
+    stok = p.stride_tok;
+    c1 = p.c1;
+    bias = p.mem_bias_raw;
+    kc = tid % TL::CPR;
+    kr0 = tid / TL::CPR;
+    va = tid % (kKT / TL::KPT);
+    vc = tid / (kKT / TL::KPT);
+    nkt = (L + kKT - 1) / kKT;
+    // first tile whose scores need the mask (memory-key bias or padding)
+    tmask = nkt;
+    if (bias != 0.0f) tmask = m / kKT;
+    if (L % kKT) tmask = min(tmask, nkt - 1);
   }
 
-  // ---- Q rows of this wave, kept in registers as the B operand of K Q^T:
-  // step s, lane half hf holds d = hf*D/2 + 8s .. +7
-  constexpr int QS = D / 16;
-  u32x4 qreg[QS];
-  const int qrow = qt * kQT + wave * kQPW + l32;
-  const bool qvalid = qrow < m;
-  const int32_t qoff = qvalid ? (FULL ? __mul24(qrow, stok) : sOff[qrow]) : 0;
-#pragma unroll
-  for (int s = 0; s < QS; ++s) {
-    qreg[s] = qvalid ? *reinterpret_cast<const u32x4*>(gq + qoff + hf * (D / 2) + s * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+  __device__ __forceinline__ uint16_t* sK(int buf) const {
+    return reinterpret_cast<uint16_t*>(smem + buf * TL::kBytes);
+  }
+  __device__ __forceinline__ uint16_t* sV(int buf) const {
+    return reinterpret_cast<uint16_t*>(smem + 2 * TL::kBytes + buf * TL::vBytes);
+  }
+  __device__ __forceinline__ int32_t* table() const {
+    return reinterpret_cast<int32_t*>(smem + TL::tileBytes);
   }
 
-  // ---- tile loader (global -> registers -> LDS).  Key indices past the end
-  // are clamped to the last key: those rows load valid data that the score
-  // mask removes, so the loader has no branches.
-  const int kc = tid % TL::CPR;                // K: chunk within a row
-  const int kr0 = tid / TL::CPR;               // K: first row
-  const int va = tid % (kKT / TL::KPT);        // V: key group
-  const int vc = tid / (kKT / TL::KPT);        // V: 8-wide d chunk
-  u32x4 kreg[TL::KPASS];
-  u32x4 vreg[TL::KPT];
-  const int Lm1 = L - 1;
+  __device__ __forceinline__ void build_table(int32_t* t, int win) const {
+    for (int r = tid; r < m; r += TL::kThreads) t[r] = window_token(p.geo, win, r) * stok;
+  }
+  // token offset of slot r of the unit's window (identity map for full attention)
+  __device__ __forceinline__ int32_t tok(const int32_t* t, int r) const {
+    return FULL ? __mul24(r, stok) : t[r];
+  }
 
-  // Keys stay below 2^24 and token offsets below 2^31 (checked on the host),
-  // so a full-rate 24-bit multiply forms the row offsets.
-  auto row_ptr = [&](int key, const uint16_t* g, const uint16_t* gm) __attribute__((always_inline)) -> const uint16_t* {
-    key = min(key, Lm1);
+  // ---- tile loader (global -> registers -> LDS).  Keys past the end are
+  // clamped to the last key: those rows load valid data that the score mask
+  // removes.  Keys stay below 2^24 and offsets below 2^31 (checked on the
+  // host), so 24-bit multiplies form the offsets.
+  __device__ __forceinline__ const uint16_t* row_ptr(const Unit& u, const int32_t* t, int key,
+                                                     bool isv) const {
+    key = min(key, L - 1);
+    const uint16_t* g = (isv ? p.v : p.k) + u.base;
     if constexpr (FULL) {
       return g + __mul24(key, stok);
     } else {
+      const uint16_t* gm = (isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D;
       const bool inwin = key < m;
-      const int32_t off = sOff[inwin ? key : 0];
+      const int32_t off = t[inwin ? key : 0];
       const int64_t moff = (int64_t)__mul24(inwin ? 0 : key - m, D);
       return inwin ? g + off : gm + moff;
     }
-  };
-  auto load_k = [&](int t) __attribute__((always_inline)) {
+  }
+  // Whole-tile address paths: tiles of window keys read the offset table,
+  // tiles of memory keys are plain rows; only tiles straddling the window /
+  // memory boundary or the end take the general per-row selects.
+  template <int N>
+  __device__ __forceinline__ void load_rows(u32x4 (&dst)[N], const Unit& u, const int32_t* t,
+                                            int tile, int r0, int rstep, int chunk,
+                                            bool isv) const {
+    const int k0 = tile * kKT;
+    if constexpr (!FULL) {
+      if (k0 + kKT <= m) {
+        const uint16_t* g = (isv ? p.v : p.k) + u.base + chunk * 8;
 #pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i)
-      kreg[i] = *reinterpret_cast<const u32x4*>(row_ptr(t * kKT + kr0 + i * TL::RPP, gk, gkm) + kc * 8);
-  };
-  auto load_v = [&](int t) __attribute__((always_inline)) {
+        for (int i = 0; i < N; ++i)
+          dst[i] = *reinterpret_cast<const u32x4*>(g + t[k0 + r0 + i * rstep]);
+        return;
+      }
+      if (k0 >= m && k0 + kKT <= L) {
+        const uint16_t* gm =
+            (isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D + (k0 - m) * D + chunk * 8;
 #pragma unroll
-    for (int i = 0; i < TL::KPT; ++i)
-      vreg[i] = *reinterpret_cast<const u32x4*>(row_ptr(t * kKT + va * TL::KPT + i, gv, gvm) + vc * 8);
-  };
-  auto store_k = [&](int buf) __attribute__((always_inline)) {
+        for (int i = 0; i < N; ++i)
+          dst[i] = *reinterpret_cast<const u32x4*>(gm + __mul24(r0 + i * rstep, D));
+        return;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      dst[i] = *reinterpret_cast<const u32x4*>(row_ptr(u, t, k0 + r0 + i * rstep, isv) +
+                                               chunk * 8);
+  }
+  __device__ __forceinline__ void load_k(const Unit& u, const int32_t* t, int tile) {
+    load_rows(kreg, u, t, tile, kr0, TL::RPP, kc, false);
+  }
+  __device__ __forceinline__ void load_k_to(u32x4 (&dst)[TL::KPASS], const Unit& u,
+                                            const int32_t* t, int tile) const {
+    load_rows(dst, u, t, tile, kr0, TL::RPP, kc, false);
+  }
+  __device__ __forceinline__ void load_v(const Unit& u, const int32_t* t, int tile) {
+    load_rows(vreg, u, t, tile, va * TL::KPT, 1, vc, true);
+  }
+  __device__ __forceinline__ void store_k_from(const u32x4 (&src)[TL::KPASS], int buf) const {
     uint16_t* dst = sK(buf);
 #pragma unroll
     for (int i = 0; i < TL::KPASS; ++i)
-      *reinterpret_cast<u32x4*>(dst + (kr0 + i * TL::RPP) * TL::KS + kc * 8) = kreg[i];
-  };
-  auto store_v = [&](int buf) __attribute__((always_inline)) {
-    // transpose: for each of the 8 d of this chunk, the KPT keys side by side
+      *reinterpret_cast<u32x4*>(dst + (kr0 + i * TL::RPP) * TL::KS + kc * 8) = src[i];
+  }
+  __device__ __forceinline__ void store_k(int buf) const { store_k_from(kreg, buf); }
+  // transpose: for each of the 8 d of this thread's chunk, its KPT keys side by side
+  __device__ __forceinline__ void store_v(int buf) const {
     uint16_t* dst = sV(buf);
     const int slot = vslot(va * TL::KPT);
 #pragma unroll
@@ -182,145 +240,240 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_bf16_kernel(AttnParams p
         dst[(vc * 8 + 2 * e + 1) * TL::VS + slot] = (uint16_t)(vreg[0][e] >> 16);
       }
     }
-  };
+  }
 
-  // ---- online softmax state (one query per lane pair)
-  constexpr int DB = D / 32;
-  f32x16 acc[DB];
+  // ---- query rows of block qb: row wave*kQPW + 32*qb + l32 of the unit
+  __device__ __forceinline__ int qrow(const Unit& u, int qb) const {
+    return u.qt * TL::kQT + wave * TL::kQPW + 32 * qb + l32;
+  }
+  // Q rows as B operand: step s, lane half hf holds d = hf*D/2 + 8s .. +7
+  __device__ __forceinline__ void load_q(const Unit& u, int qb, int32_t qoff, bool qvalid) {
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-  float m_used = -INFINITY;   // running max in log2 units (may lag by < slack)
-  float l_part = 0.0f;        // this lane's share of the row sum (two partial sums)
-  float l_part1 = 0.0f;
-  const float c1 = p.c1;
-  const float bias = p.mem_bias_raw;
-  const f32x16 zero16 = {};
+    for (int s = 0; s < QS; ++s)
+      qreg[qb][s] = qvalid
+          ? *reinterpret_cast<const u32x4*>(p.q + u.base + qoff + hf * (D / 2) + s * 8)
+          : u32x4{0u, 0u, 0u, 0u};
+  }
 
-  auto compute_s = [&](const uint16_t* kt, f32x16 (&s)[2]) {
+  // ---- softmax pieces
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int ss = 0; ss < QS; ++ss) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(
-            kt + (kb * 32 + l32) * TL::KS + hf * (D / 2) + ss * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qreg[ss]),
-            ss == 0 ? zero16 : s[kb], 0, 0, 0);
-      }
-    }
-  };
-  // padding keys -> -inf; memory keys get the logit bias (selects, no branches)
-  auto mask_s = [&](f32x16 (&s)[2], int k0) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const float x = s[kb][r] + (key >= m ? bias : 0.0f);
-        s[kb][r] = key < L ? x : -INFINITY;
-      }
-  };
-  auto rowmax = [&](const f32x16 (&s)[2]) -> float {
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                     false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  };
-  // lagging max: rescale O only when the max has grown by more than the slack
-  auto update_max = [&](float mx) __attribute__((always_inline)) {
-    const float m_new = mx * c1;
-    const bool need = m_new > m_used + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_tgt = need ? m_new : m_used;
-      const float alpha = exp2f(m_used - m_tgt);
-      m_used = m_tgt;
-      l_part *= alpha;
-      l_part1 *= alpha;
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.0f;
+      m_used[qb] = -INFINITY;
+      l0[qb] = 0.0f;
+      l1[qb] = 0.0f;
     }
-  };
-  // P = exp2(S*c1 - m): row sum (two partial sums) and the bf16 operands of
-  // the P V product
-  auto make_p = [&](const f32x16 (&s)[2], u32x4 (&pb)[4]) {
-    const float nm = -m_used;
+  }
+  __device__ __forceinline__ void compute_s(const uint16_t* kt, Scores& s) const {
+    const f32x16 zero16 = {};
+    // step-major: the KB independent accumulator chains alternate, so each
+    // LDS operand read has a few MFMAs of slack and no MFMA waits on the last
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int ss = 0; ss < QS; ++ss) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float e[8];
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(
+            kt + (kb * 32 + l32) * TL::KS + hf * (D / 2) + ss * 8);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * u + j], c1, nm));
-        u32x4 w{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
-        float& lp = u ? l_part1 : l_part;
-        lp += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        pb[2 * kb + u] = w;
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qreg[qb][ss]),
+              ss == 0 ? zero16 : s[qb][kb], 0, 0, 0);
       }
     }
-  };
-  // O^T += V^T P^T
-  auto pv = [&](const uint16_t* vt, const u32x4 (&pb)[4]) {
+  }
+  // padding keys -> -inf; memory keys get the logit bias (selects, no branches)
+  __device__ __forceinline__ void mask_s(Scores& s, int k0) const {
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float x = s[qb][kb][r] + (key >= m ? bias : 0.0f);
+          s[qb][kb][r] = key < L ? x : -INFINITY;
+        }
+  }
+  __device__ __forceinline__ float rowmax(const Scores& s, int qb) const {
+    float mx = s[qb][0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  __device__ __forceinline__ void rowmax_all(const Scores& s, float (&mx)[QB]) const {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = rowmax(s, qb);
+  }
+  // lagging max: rescale O only when the max has grown by more than the slack
+  __device__ __forceinline__ void update_max(const float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = mx[qb] * c1;
+      const bool need = m_new > m_used[qb] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_tgt = need ? m_new : m_used[qb];
+        const float alpha = exp2f(m_used[qb] - m_tgt);
+        m_used[qb] = m_tgt;
+        l0[qb] *= alpha;
+        l1[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][i][r] *= alpha;
+      }
+    }
+  }
+  // P = exp2(S*c1 - m): row sums (two partial sums) and the bf16 operands of
+  // the P V product
+  __device__ __forceinline__ void make_p(const Scores& s, Probs& pb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m_used[qb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * u + j], c1, nm));
+          const float sum = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          if (u) l1[qb] += sum;
+          else l0[qb] += sum;
+          pb[qb][2 * kb + u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                                     pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+        }
+      }
+    }
+  }
+  // O^T += V^T P^T
+  __device__ __forceinline__ void pv(const uint16_t* vt, const Probs& pb) {
+#pragma unroll
+    for (int sl = 0; sl < 2 * KB; ++sl) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(
             vt + (db * 32 + l32) * TL::VS + sl * 16 + hf * 8);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[sl]), acc[db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb[qb][sl]),
+              acc[qb][db], 0, 0, 0);
       }
     }
-  };
+  }
+  // normalise and scatter query block qb back to raster order
+  __device__ __forceinline__ void finish(const Unit& u, int qb, int32_t qoff, bool qvalid) const {
+    const float lp = l0[qb] + l1[qb];
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
+                                                     false, false);
+    const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+    if (qvalid) {
+      uint16_t* dst = p.out + u.base + qoff;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hf;
+          const u32x2 w{pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv),
+                        pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(dst + d) = w;
+        }
+    }
+  }
+};
 
-  // first tile whose scores need the mask (memory-key bias or padding)
-  const int nkt = (L + kKT - 1) / kKT;
-  int tmask = nkt;
-  if (bias != 0.0f) tmask = m / kKT;
-  if (L % kKT) tmask = min(tmask, nkt - 1);
+// One workgroup per work unit.
+template <int D, bool FULL, int NW, int QB, int KT>
+__global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) attn_bf16_kernel(AttnParams p) {
+  using C = Core<D, FULL, NW, QB, KT>;
+  constexpr int kKT = KT;
+  using Scores = typename C::Scores;
+  using Probs = typename C::Probs;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // ---- prologue: K(0), V(0), K(1) in LDS; V(1), K(2) in flight
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  load_k(1);
-  store_k(1);
-  __syncthreads();
-  load_v(1);
-  load_k(2);
-  f32x16 sA[2], sB[2];
-  compute_s(sK(0), sA);
-  if (tmask == 0) mask_s(sA, 0);
-  update_max(rowmax(sA));
+  // XCD-aware: consecutive units run on one XCD's L2
+  const int xcd = blockIdx.x & 7;
+  const int kidx = blockIdx.x >> 3;
+  const int unit = xcd * p.units_per_xcd + kidx;
+  if (kidx >= p.units_per_xcd || unit >= p.units) return;
 
-  // ---- steady state.  Iteration t: S(t+1) from K buffer (t+1)&1 while P(t)
-  // is formed; P(t) V(t) from V buffer t&1 while max S(t+1) is taken; then
-  // V(t+1) and K(t+2) go to the buffers that iteration t-1 finished with.
-  // The two score buffers alternate roles, so the loop runs in pairs.
-  auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    u32x4 pb[4];
-    compute_s(sK((t + 1) & 1), sn);
-    make_p(sc, pb);
-    pv(sV(t & 1), pb);
-    if constexpr (MASK) mask_s(sn, (t + 1) * kKT);
-    const float mx = rowmax(sn);
-    store_v((t + 1) & 1);
-    store_k(t & 1);
+  C c(p, smem);
+  const Unit u = decode_unit(p, unit);
+  int32_t* tab = c.table();
+  if (!FULL) {
+    c.build_table(tab, u.win);
     __syncthreads();
-    load_v(t + 2);
-    load_k(t + 3);
-    update_max(mx);
+  }
+  int32_t qoff[QB];
+  bool qvalid[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = c.qrow(u, qb);
+    qvalid[qb] = r < c.m;
+    qoff[qb] = qvalid[qb] ? c.tok(tab, r) : 0;
+    c.load_q(u, qb, qoff[qb], qvalid[qb]);
+  }
+  c.reset();
+  const int nkt = c.nkt;
+
+  // prologue: K(0), V(0), K(1) loaded together (with Q) and stored; V(1),
+  // K(2) then stay in flight
+  {
+    u32x4 k1[C::TL::KPASS];
+    c.load_k(u, tab, 0);
+    c.load_v(u, tab, 0);
+    c.load_k_to(k1, u, tab, 1);
+    c.store_k(0);
+    c.store_v(0);
+    c.store_k_from(k1, 1);
+  }
+  __syncthreads();
+  c.load_v(u, tab, 1);
+  c.load_k(u, tab, 2);
+  Scores sA, sB;
+  float mx[QB];
+  c.compute_s(c.sK(0), sA);
+  if (c.tmask == 0) c.mask_s(sA, 0);
+  c.rowmax_all(sA, mx);
+  c.update_max(mx);
+  __syncthreads();  // every wave is done with K(0) before iteration 0 refills its buffer
+
+  // Iteration t: S(t+1) from K buffer (t+1)&1 while P(t) is formed; P(t) V(t)
+  // from V buffer t&1 while max S(t+1) is taken; then V(t+1) and K(t+2) go
+  // to the buffers that iteration t-1 finished with.
+  auto iter = [&](int t, Scores& sc, Scores& sn, auto masked) __attribute__((always_inline)) {
+    Probs pb;
+    float mxn[QB];
+    c.compute_s(c.sK((t + 1) & 1), sn);
+    c.make_p(sc, pb);
+    c.pv(c.sV(t & 1), pb);
+    if constexpr (decltype(masked)::value) c.mask_s(sn, (t + 1) * kKT);
+    c.rowmax_all(sn, mxn);
+    c.store_v((t + 1) & 1);
+    c.store_k(t & 1);
+    __syncthreads();
+    c.load_v(u, tab, t + 2);
+    c.load_k(u, tab, t + 3);
+    c.update_max(mxn);
+  };
+  auto copy = [&](Scores& dst, const Scores& src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) dst[qb][kb] = src[qb][kb];
   };
   int t = 0;
-  const int t1 = min(nkt, tmask);  // iterations t < t1 - 1 need no mask on S(t+1)
+  const int t1 = min(nkt, c.tmask);  // iterations t < t1 - 1 need no mask on S(t+1)
   for (; t + 2 < t1; t += 2) {
     iter(t, sA, sB, bool_c<false>{});
     iter(t + 1, sB, sA, bool_c<false>{});
@@ -328,8 +481,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_bf16_kernel(AttnParams p
   if (t + 1 < t1) {
     iter(t, sA, sB, bool_c<false>{});
     ++t;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+    copy(sA, sB);
   }
   for (; t + 2 < nkt; t += 2) {
     iter(t, sA, sB, bool_c<true>{});
@@ -338,68 +490,62 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_bf16_kernel(AttnParams p
   if (t + 1 < nkt) {
     iter(t, sA, sB, bool_c<true>{});
     ++t;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+    copy(sA, sB);
   }
   {
-    u32x4 pb[4];
-    make_p(sA, pb);
-    pv(sV(t & 1), pb);
+    Probs pb;
+    c.make_p(sA, pb);
+    c.pv(c.sV(t & 1), pb);
   }
-
-  // ---- normalise and scatter back to raster order
-  {
-    const float lp = l_part + l_part1;
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
-                                                     false, false);
-    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const float inv = 1.0f / l;
-    if (qvalid) {
-      uint16_t* dst = go + qoff;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hf;
-          const u32x2 w{pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                        pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + d) = w;
-        }
-    }
-  }
+  for (int qb = 0; qb < QB; ++qb) c.finish(u, qb, qoff[qb], qvalid[qb]);
 }
 
-template <int D, bool FULL, int NW>
+
+// Workgroup shape: NW waves of QB query blocks (32 rows each).
+#ifndef BASA_ATTN_WAVES
+#define BASA_ATTN_WAVES 8
+#endif
+#ifndef BASA_ATTN_QBLOCKS
+#define BASA_ATTN_QBLOCKS 1
+#endif
+#ifndef BASA_ATTN_KTILE
+#define BASA_ATTN_KTILE 64
+#endif
+template <typename K>
+int set_lds_limit(K kernel, bool& done) {
+  if (done) return BASA_OK;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+    return BASA_ERR_HIP;
+  done = true;  // benign race: the call is idempotent
+  return BASA_OK;
+}
+
+template <int D, bool FULL, int NW, int QB, int KT>
 int launch(const AttnParams& p0, hipStream_t stream) {
-  using TL = Tiles<D, NW>;
+  using TL = Tiles<D, NW, QB, KT>;
   AttnParams p = p0;
   p.nQT = (p.m + TL::kQT - 1) / TL::kQT;
   const int64_t units = (int64_t)p.batch_heads * p.nW * p.nQT;
   if (units > (int64_t)INT32_MAX / 2) return BASA_ERR_UNSUPPORTED;
   p.units = (int32_t)units;
   p.units_per_xcd = (p.units + 7) / 8;
-  const size_t lds = TL::ldsBytes + (FULL ? 0 : (size_t)p.m * 4);
+  const size_t lds = TL::tileBytes + (FULL ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
-  static bool attr_set = false;  // benign race: the call is idempotent
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D, FULL, NW>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return BASA_ERR_HIP;
-    attr_set = true;
-  }
-  const dim3 grid((unsigned)(8 * p.units_per_xcd));
-  hipLaunchKernelGGL((attn_bf16_kernel<D, FULL, NW>), grid, dim3(TL::kThreads), lds, stream, p);
+  static bool attr = false;
+  if (set_lds_limit(&attn_bf16_kernel<D, FULL, NW, QB, KT>, attr)) return BASA_ERR_HIP;
+  hipLaunchKernelGGL((attn_bf16_kernel<D, FULL, NW, QB, KT>), dim3((unsigned)(8 * p.units_per_xcd)),
+                     dim3(TL::kThreads), lds, stream, p);
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
-#ifndef BASA_ATTN_WAVES
-#define BASA_ATTN_WAVES 8
-#endif
-
 template <int D>
 int launch_d(const AttnParams& p, bool full, hipStream_t stream) {
-  return full ? launch<D, true, BASA_ATTN_WAVES>(p, stream)
-              : launch<D, false, BASA_ATTN_WAVES>(p, stream);
+  // a head dim of 64 needs 64-key tiles to give every thread of 8 waves work
+  constexpr int KT = (D == 64 && BASA_ATTN_KTILE * D < 64 * 64) ? 64 : BASA_ATTN_KTILE;
+  return full ? launch<D, true, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream)
+              : launch<D, false, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream);
 }
 
 }  // namespace

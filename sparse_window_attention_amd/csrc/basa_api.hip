@@ -33,6 +33,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// NaN or infinity, from the bit pattern (no compiler flag can fold this away)
+bool not_finite(float x) {
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  return (b & 0x7f800000u) == 0x7f800000u;
+}
+
 struct Grid3 {
   int32_t g[3];
   int64_t n;
@@ -214,8 +221,8 @@ int basa_window_attn(const void* q, const void* k, const void* v, const void* k_
     if (k_mem && (n_mem < 1 || n_mem > (1 << 20)))
       return fail(BASA_ERR_INVALID_ARG, "n_mem must be in [1, 2^20] with memory (got %lld)", (long long)n_mem);
     if (!k_mem && n_mem != 0) return fail(BASA_ERR_INVALID_ARG, "n_mem must be 0 without memory");
-    if (isnan(scale) || isinf(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
-    if (isnan(mem_bias) || isinf(mem_bias)) return fail(BASA_ERR_INVALID_ARG, "mem_bias must be finite");
+    if (not_finite(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (not_finite(mem_bias)) return fail(BASA_ERR_INVALID_ARG, "mem_bias must be finite");
     const int64_t m = (int64_t)w[0] * w[1] * w[2];
     if (m > BASA_MAX_WINDOW_TOKENS)
       return fail(BASA_ERR_UNSUPPORTED, "window of %lld tokens exceeds %d", (long long)m, BASA_MAX_WINDOW_TOKENS);
@@ -271,7 +278,7 @@ int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
     if (n_tokens < 1) return fail(BASA_ERR_INVALID_ARG, "n_tokens must be >= 1");
-    if (isnan(scale) || isinf(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (not_finite(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
       return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
     int64_t sb, sh, stok;

@@ -7,11 +7,13 @@
 // covers; memory tokens are stored [B, H, G, D] in raster order of the pooled
 // grid.
 //
-// A streaming reduction bound by HBM bandwidth: each thread owns one 16-byte
-// chunk of one memory token for both K and V and walks the tokens of its
-// cell.  The lanes of a wave cover whole 16-byte-chunk rows of neighbouring
-// cells, so every load instruction reads full token rows.  fp32 accumulation;
-// bf16 results rounded to nearest even.
+// A streaming reduction bound by HBM bandwidth.  One wave per (batch, head,
+// cell): the CPR lanes of a lane group hold the 16-byte chunks of one token
+// row (so every load instruction reads whole rows), and the 64 / CPR lane
+// groups split the cell's pt*py grid rows between them.  Each lane walks the
+// px tokens of its rows for K and V, then the groups' partial sums are added
+// with lane exchanges.  fp32 accumulation; bf16 results rounded to nearest
+// even.
 #include "basa_common.h"
 #include "basa_internal.h"
 
@@ -19,82 +21,82 @@ namespace basa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = 4;
 
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) pool_kernel(PoolParams p, int64_t total) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= total) return;
-  constexpr int EPC = BF16 ? 8 : 4;           // elements per 16B chunk
-  const int cpr = p.head_dim / EPC;           // chunks per row
-  const int chunk = (int)(gid % cpr);
-  const int64_t rest = gid / cpr;
-  const int g = (int)(rest % p.G);
-  const int bh = (int)(rest / p.G);
+__device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4& x) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_lo(x[e]);
+      acc[2 * e + 1] += bf16_hi(x[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(x[e]);
+  }
+}
+
+template <bool BF16, int CPR>
+__global__ void __launch_bounds__(kWavesPerBlock * 64) pool_kernel(PoolParams p, int64_t cells) {
+  constexpr int EPC = BF16 ? 8 : 4;   // elements per 16B chunk
+  constexpr int NG = 64 / CPR;        // lane groups (row splits) per wave
+  constexpr int NA = EPC;             // live accumulators per tensor
+  const int64_t cell = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (cell >= cells) return;          // whole wave exits together
+  const int lane = threadIdx.x & 63;
+  const int chunk = lane % CPR;
+  const int grp = lane / CPR;
+  const int g = (int)(cell % p.G);
+  const int bh = (int)(cell / p.G);
   const int b = bh / p.heads, h = bh - b * p.heads;
   const int gx = g % p.Gx;
   const int gy = (g / p.Gx) % p.Gy;
   const int gt = g / (p.Gx * p.Gy);
   const int64_t base = (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
-  const int esz = BF16 ? 2 : 4;
-  const char* kb = reinterpret_cast<const char*>(p.k) + (base + chunk * EPC) * esz;
-  const char* vb = reinterpret_cast<const char*>(p.v) + (base + chunk * EPC) * esz;
-  const int64_t tokb = (int64_t)p.stride_tok * esz;
+  constexpr int ES = BF16 ? 2 : 4;
+  const char* kb = reinterpret_cast<const char*>(p.k) + (base + chunk * EPC) * ES;
+  const char* vb = reinterpret_cast<const char*>(p.v) + (base + chunk * EPC) * ES;
+  const int64_t tokb = (int64_t)p.stride_tok * ES;
 
-  float ks[8] = {0, 0, 0, 0, 0, 0, 0, 0}, vs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int a = 0; a < p.pt; ++a) {
-    for (int c = 0; c < p.py; ++c) {
-      const int64_t row = ((int64_t)(gt * p.pt + a) * p.Hg + (gy * p.py + c)) * p.Wg + gx * p.px;
-      const char* kr = kb + row * tokb;
-      const char* vr = vb + row * tokb;
-      int x = 0;
-      for (; x + 4 <= p.px; x += 4) {
-        u32x4 kk[4], vv[4];
+  float ks[8], vs[8];  // the first NA are live
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          kk[u] = *reinterpret_cast<const u32x4*>(kr + (x + u) * tokb);
-          vv[u] = *reinterpret_cast<const u32x4*>(vr + (x + u) * tokb);
-        }
+  for (int e = 0; e < 8; ++e) ks[e] = vs[e] = 0.0f;
+  const int rows = p.pt * p.py;       // grid rows of the cell, split over lane groups
+  for (int rr = grp; rr < rows; rr += NG) {
+    const int a = rr / p.py, c = rr - a * p.py;
+    const int64_t row = ((int64_t)(gt * p.pt + a) * p.Hg + (gy * p.py + c)) * p.Wg + gx * p.px;
+    const char* kr = kb + row * tokb;
+    const char* vr = vb + row * tokb;
+    int x = 0;
+    for (; x + 4 <= p.px; x += 4) {
+      u32x4 kk[4], vv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if constexpr (BF16) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ks[2 * e] += bf16_lo(kk[u][e]);
-              ks[2 * e + 1] += bf16_hi(kk[u][e]);
-              vs[2 * e] += bf16_lo(vv[u][e]);
-              vs[2 * e + 1] += bf16_hi(vv[u][e]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ks[e] += __uint_as_float(kk[u][e]);
-              vs[e] += __uint_as_float(vv[u][e]);
-            }
-          }
-        }
+      for (int u = 0; u < 4; ++u) {
+        kk[u] = *reinterpret_cast<const u32x4*>(kr + (x + u) * tokb);
+        vv[u] = *reinterpret_cast<const u32x4*>(vr + (x + u) * tokb);
       }
-      for (; x < p.px; ++x) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(kr + x * tokb);
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vr + x * tokb);
-        if constexpr (BF16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ks[2 * e] += bf16_lo(kk[e]);
-            ks[2 * e + 1] += bf16_hi(kk[e]);
-            vs[2 * e] += bf16_lo(vv[e]);
-            vs[2 * e + 1] += bf16_hi(vv[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ks[e] += __uint_as_float(kk[e]);
-            vs[e] += __uint_as_float(vv[e]);
-          }
-        }
+      for (int u = 0; u < 4; ++u) {
+        accumulate<BF16>(ks, kk[u]);
+        accumulate<BF16>(vs, vv[u]);
       }
     }
+    for (; x < p.px; ++x) {
+      accumulate<BF16>(ks, *reinterpret_cast<const u32x4*>(kr + x * tokb));
+      accumulate<BF16>(vs, *reinterpret_cast<const u32x4*>(vr + x * tokb));
+    }
   }
+  // add the lane groups' partial sums: groups differ in the lane bits above CPR
+#pragma unroll
+  for (int off = CPR; off < 64; off *= 2) {
+#pragma unroll
+    for (int e = 0; e < NA; ++e) {
+      ks[e] += __shfl_xor(ks[e], off);
+      vs[e] += __shfl_xor(vs[e], off);
+    }
+  }
+  if (grp != 0) return;
   const float cnt = (float)(p.pt * p.py * p.px);
   const int64_t obase = ((int64_t)bh * p.G + g) * p.head_dim + chunk * EPC;
   if constexpr (BF16) {
@@ -114,18 +116,29 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(PoolParams p, int64_t to
   }
 }
 
+template <bool BF16, int CPR>
+int launch_cpr(const PoolParams& p, hipStream_t stream) {
+  const int64_t cells = (int64_t)p.batch_heads * p.G;
+  const int64_t blocks = (cells + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > INT32_MAX) return BASA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((pool_kernel<BF16, CPR>), dim3((unsigned)blocks), dim3(kWavesPerBlock * 64), 0,
+                     stream, p, cells);
+  return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
 }  // namespace
 
 int launch_pool(const PoolParams& p, int dtype, hipStream_t stream) {
   const bool bf16 = dtype == BASA_BF16;
-  const int64_t total = (int64_t)p.batch_heads * p.G * (p.head_dim / (bf16 ? 8 : 4));
-  const int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > INT32_MAX) return BASA_ERR_UNSUPPORTED;
-  if (bf16)
-    hipLaunchKernelGGL(pool_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, total);
-  else
-    hipLaunchKernelGGL(pool_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, total);
-  return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+  const int cpr = p.head_dim * (bf16 ? 2 : 4) / 16;  // 16B chunks per token row
+  if (bf16) {
+    if (cpr == 16) return launch_cpr<true, 16>(p, stream);
+    if (cpr == 8) return launch_cpr<true, 8>(p, stream);
+  } else {
+    if (cpr == 32) return launch_cpr<false, 32>(p, stream);
+    if (cpr == 16) return launch_cpr<false, 16>(p, stream);
+  }
+  return BASA_ERR_UNSUPPORTED;
 }
 
 }  // namespace basa
