@@ -46,9 +46,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=("window", "dense", "all"), default="all",
+    ap.add_argument("--only", choices=("window", "dense", "copy", "all"), default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
-                         "at the same shape (for profilers)")
+                         "at the same shape; 'copy': a plain device copy of known size, the "
+                         "calibration for hardware byte counters (all three for profilers)")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="no GPU: read rocprofv3 outputs under DIR (ktrace/, pmc_fetch/, "
+                         "pmc_write/, pmc_copy_fetch/, pmc_copy_write/), write the calibrated "
+                         "HBM traffic of the attention kernel and print the summaries")
     return ap.parse_args()
 
 
@@ -140,6 +145,100 @@ def time_dense(S, sets, reps, stream):
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))
     return ts
+
+
+COPY_BYTES = 1 << 30   # bytes read (and again written) by one calibration copy
+
+
+def time_copy(reps, stream):
+    """A plain device-to-device copy of COPY_BYTES, the known-size reference that
+    FETCH_SIZE / WRITE_SIZE are scaled by."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return ts
+
+
+def _counter_means(path, counter):
+    """{kernel name: mean counter value per dispatch} from a rocprofv3 csv."""
+    import csv
+    import glob
+    tot, disp = {}, {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def _pick(d, key):
+    hits = {k: v for k, v in d.items() if key in k}
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {key!r}, found {list(hits)}")
+    return next(iter(hits.items()))
+
+
+def summarize_profiles(root):
+    """Turns the byte-counter runs into calibrated HBM bytes per attention launch.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by
+    the ratio of the true bytes to what the same counter reads for the plain
+    copy of COPY_BYTES."""
+    import workloads as W
+    wl = W.FLUX2048_W16
+    copy_f = _pick(_counter_means(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE"), "copy")[1]
+    copy_w = _pick(_counter_means(os.path.join(root, "pmc_copy_write"), "WRITE_SIZE"), "copy")[1]
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    fetch = _counter_means(os.path.join(root, "pmc_fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(root, "pmc_write"), "WRITE_SIZE")
+    out = {"workload": wl.name, "kernel_source_hash": kernel_hash(),
+           "copy_bytes": COPY_BYTES,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    B, H, n, D, G = wl.batch, wl.heads, wl.n_tokens, wl.head_dim, wl.mem_tokens
+    algo = {"attn_bf16": (3 * B * H * n * D * 2 + 2 * B * H * G * D * 2, B * H * n * D * 2),
+            "pool_kernel": (2 * B * H * n * D * 2, 2 * B * H * G * D * 2)}
+    for key, (ar, aw) in algo.items():
+        name, fk = _pick(fetch, key)
+        _, wk = _pick(write, key)
+        rd, wr = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
+        out["kernels"][key] = {"name": name, "fetch_kib": fk, "write_kib": wk,
+                               "read_bytes": rd, "write_bytes": wr,
+                               "algorithmic_read_bytes": ar, "algorithmic_write_bytes": aw,
+                               "read_over_algorithmic": rd / ar,
+                               "write_over_algorithmic": wr / aw}
+    a = out["kernels"]["attn_bf16"]
+    out["hbm_bytes_per_launch"] = a["read_bytes"] + a["write_bytes"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    stats = os.path.join(root, "ktrace")
+    import csv
+    import glob
+    for f in glob.glob(os.path.join(stats, "**", "*kernel_stats.csv"), recursive=True):
+        print(f"\nkernel stats ({os.path.relpath(f, root)}):")
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                print(f"  {r['Name'][:90]:90s} calls {r['Calls']:>5s} avg_us "
+                      f"{float(r['AverageNs']) / 1e3:9.2f} min_us {float(r['MinNs']) / 1e3:9.2f} "
+                      f"max_us {float(r['MaxNs']) / 1e3:9.2f} pct {float(r['Percentage']):6.2f}")
 
 
 def median(x):
@@ -243,6 +342,9 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -262,6 +364,11 @@ def main():
         sets = make_sets(head, 1, dev)
         ts = time_dense(S, sets, args.steps, stream)
         print(json.dumps({"dense_ms": median(ts)}))
+        return
+    if args.only == "copy":
+        ts = time_copy(args.steps, stream)
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copy_ms": median(ts),
+                          "copy_gbs": 2 * COPY_BYTES / (median(ts) * 1e-3) / 1e9}))
         return
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
