@@ -18,6 +18,15 @@
 // K(t+1) Q^T, and the row max of tile t+1 overlaps the P V product of tile
 // t.  K runs one tile ahead of V through two LDS buffers each.
 //
+// Two kernels share this core.  The unit kernel runs one workgroup per work
+// unit.  The persistent kernel (used when a unit has at least
+// kPersistentMinTiles tiles and its LDS fits) runs one workgroup per CU that
+// walks a list of units of one XCD with the same tile loop.  While a unit
+// runs, the next unit's Q rows and first three K/V tiles are copied into an
+// LDS staging area by direct global-to-LDS loads spread over the iterations,
+// so the next unit starts from LDS instead of paying a burst of HBM loads,
+// and the finished unit's output stores drain while the next one computes.
+//
 // The cyclic shift and the window gather are address arithmetic: a table of
 // the window's raster offsets is built in LDS per unit and every Q/K/V/O row
 // is addressed through it (BASA forum summary, "The BASA Method": shift,
@@ -34,6 +43,7 @@ namespace basa {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
+constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel needs
 
 template <int D, int NW, int QB, int KT>
 struct Tiles {
@@ -66,6 +76,18 @@ __device__ __forceinline__ int vslot(int key) {
 
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
+
+// Raw buffer resource over a (batch, head) slice: wave-uniform base in
+// scalar registers, per-lane 32-bit byte offsets (every offset inside a slice
+// is below 2^32 bytes, checked on the host).
+using Rsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFFu,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
 
 // One work unit: element offset of its (batch, head) slice in Q/K/V/O, its
 // (batch, head) index, window and query tile.
@@ -102,7 +124,8 @@ struct Core {
   const AttnParams& p;
   unsigned char* smem;
   int tid, wave, l32, hf;
-  int m, L, stok, tmask, nkt;
+  int m, L, tmask, nkt;
+  uint32_t stb;                       // bytes between tokens
   float c1, bias;
   int kc, kr0, va, vc;                // tile loader geometry
   u32x4 qreg[QB][QS];                 // Q rows (B operand of K Q^T)
@@ -120,7 +143,7 @@ struct Core {
     hf = lane >> 5;
     m = p.m;
     L = m + p.G;
-    stok = p.stride_tok;
+    stb = (uint32_t)p.stride_tok * 2u;
     c1 = p.c1;
     bias = p.mem_bias_raw;
     kc = tid % TL::CPR;
@@ -134,80 +157,90 @@ struct Core {
     if (L % kKT) tmask = min(tmask, nkt - 1);
   }
 
+  // Marks the per-lane indices as redefined here.  Addresses derived from
+  // them are then formed after this point instead of being hoisted out of an
+  // enclosing loop and held in registers through it.
+  __device__ __forceinline__ void redefine_lane_ids() {
+    asm volatile("" : "+v"(tid), "+v"(l32), "+v"(hf), "+v"(kc), "+v"(kr0), "+v"(va), "+v"(vc));
+    asm volatile("" : "+s"(m), "+s"(L), "+s"(stb), "+s"(c1), "+s"(bias));
+  }
+
   __device__ __forceinline__ uint16_t* sK(int buf) const {
     return reinterpret_cast<uint16_t*>(smem + buf * TL::kBytes);
   }
   __device__ __forceinline__ uint16_t* sV(int buf) const {
     return reinterpret_cast<uint16_t*>(smem + 2 * TL::kBytes + buf * TL::vBytes);
   }
-  __device__ __forceinline__ int32_t* table() const {
-    return reinterpret_cast<int32_t*>(smem + TL::tileBytes);
+  __device__ __forceinline__ uint32_t* table() const {
+    return reinterpret_cast<uint32_t*>(smem + TL::tileBytes);
   }
 
-  __device__ __forceinline__ void build_table(int32_t* t, int win) const {
-    for (int r = tid; r < m; r += TL::kThreads) t[r] = window_token(p.geo, win, r) * stok;
+  // byte offsets of the window's tokens inside the (batch, head) slice
+  __device__ __forceinline__ void build_table(uint32_t* t, int win) const {
+    for (int r = tid; r < m; r += TL::kThreads) t[r] = (uint32_t)window_token(p.geo, win, r) * stb;
   }
-  // token offset of slot r of the unit's window (identity map for full attention)
-  __device__ __forceinline__ int32_t tok(const int32_t* t, int r) const {
-    return FULL ? __mul24(r, stok) : t[r];
+  // byte offset of slot r of the unit's window (identity map for full attention)
+  __device__ __forceinline__ uint32_t tok(const uint32_t* t, int r) const {
+    return FULL ? (uint32_t)r * stb : t[r];
   }
 
   // ---- tile loader (global -> registers -> LDS).  Keys past the end are
   // clamped to the last key: those rows load valid data that the score mask
   // removes.  Keys stay below 2^24 and offsets below 2^31 (checked on the
   // host), so 24-bit multiplies form the offsets.
-  __device__ __forceinline__ const uint16_t* row_ptr(const Unit& u, const int32_t* t, int key,
-                                                     bool isv) const {
+  __device__ __forceinline__ const char* row_ptr(const Unit& u, const uint32_t* t, int key,
+                                                  bool isv) const {
     key = min(key, L - 1);
-    const uint16_t* g = (isv ? p.v : p.k) + u.base;
-    if constexpr (FULL) {
-      return g + __mul24(key, stok);
-    } else {
-      const uint16_t* gm = (isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D;
-      const bool inwin = key < m;
-      const int32_t off = t[inwin ? key : 0];
-      const int64_t moff = (int64_t)__mul24(inwin ? 0 : key - m, D);
-      return inwin ? g + off : gm + moff;
-    }
+    const char* g = reinterpret_cast<const char*>((isv ? p.v : p.k) + u.base);
+    if constexpr (FULL) return g + (uint32_t)key * stb;
+    const char* gm = reinterpret_cast<const char*>((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
+    const bool inwin = key < m;
+    const uint32_t off = t[inwin ? key : 0];
+    const uint32_t moff = (uint32_t)__mul24(inwin ? 0 : key - m, D * 2);
+    return inwin ? g + off : gm + moff;
   }
   // Whole-tile address paths: tiles of window keys read the offset table,
   // tiles of memory keys are plain rows; only tiles straddling the window /
   // memory boundary or the end take the general per-row selects.
   template <int N>
-  __device__ __forceinline__ void load_rows(u32x4 (&dst)[N], const Unit& u, const int32_t* t,
+  __device__ __forceinline__ void load_rows(u32x4 (&dst)[N], const Unit& u, const uint32_t* t,
                                             int tile, int r0, int rstep, int chunk,
                                             bool isv) const {
     const int k0 = tile * kKT;
-    if constexpr (!FULL) {
-      if (k0 + kKT <= m) {
-        const uint16_t* g = (isv ? p.v : p.k) + u.base + chunk * 8;
+    const uint32_t cb = (uint32_t)chunk * 16u;
+    if constexpr (FULL) {
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-          dst[i] = *reinterpret_cast<const u32x4*>(g + t[k0 + r0 + i * rstep]);
+      for (int i = 0; i < N; ++i)
+        dst[i] = buf_load16(rs, (uint32_t)min(k0 + r0 + i * rstep, L - 1) * stb + cb, 0);
+    } else {
+      if (k0 + kKT <= m) {
+        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = buf_load16(rs, t[k0 + r0 + i * rstep] + cb, 0);
         return;
       }
       if (k0 >= m && k0 + kKT <= L) {
-        const uint16_t* gm =
-            (isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D + (k0 - m) * D + chunk * 8;
+        const Rsrc rs = make_rsrc((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
+        const uint32_t so = (uint32_t)(k0 - m) * (D * 2);
 #pragma unroll
         for (int i = 0; i < N; ++i)
-          dst[i] = *reinterpret_cast<const u32x4*>(gm + __mul24(r0 + i * rstep, D));
+          dst[i] = buf_load16(rs, (uint32_t)(r0 + i * rstep) * (D * 2) + cb, so);
         return;
       }
-    }
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      dst[i] = *reinterpret_cast<const u32x4*>(row_ptr(u, t, k0 + r0 + i * rstep, isv) +
-                                               chunk * 8);
+      for (int i = 0; i < N; ++i)
+        dst[i] = *reinterpret_cast<const u32x4*>(row_ptr(u, t, k0 + r0 + i * rstep, isv) + cb);
+    }
   }
-  __device__ __forceinline__ void load_k(const Unit& u, const int32_t* t, int tile) {
+  __device__ __forceinline__ void load_k(const Unit& u, const uint32_t* t, int tile) {
     load_rows(kreg, u, t, tile, kr0, TL::RPP, kc, false);
   }
   __device__ __forceinline__ void load_k_to(u32x4 (&dst)[TL::KPASS], const Unit& u,
-                                            const int32_t* t, int tile) const {
+                                            const uint32_t* t, int tile) const {
     load_rows(dst, u, t, tile, kr0, TL::RPP, kc, false);
   }
-  __device__ __forceinline__ void load_v(const Unit& u, const int32_t* t, int tile) {
+  __device__ __forceinline__ void load_v(const Unit& u, const uint32_t* t, int tile) {
     load_rows(vreg, u, t, tile, va * TL::KPT, 1, vc, true);
   }
   __device__ __forceinline__ void store_k_from(const u32x4 (&src)[TL::KPASS], int buf) const {
@@ -247,12 +280,13 @@ struct Core {
     return u.qt * TL::kQT + wave * TL::kQPW + 32 * qb + l32;
   }
   // Q rows as B operand: step s, lane half hf holds d = hf*D/2 + 8s .. +7
-  __device__ __forceinline__ void load_q(const Unit& u, int qb, int32_t qoff, bool qvalid) {
+  __device__ __forceinline__ void load_q(const Unit& u, int qb, uint32_t qoff, bool qvalid) {
+    const Rsrc rs = make_rsrc(p.q + u.base);
 #pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qreg[qb][s] = qvalid
-          ? *reinterpret_cast<const u32x4*>(p.q + u.base + qoff + hf * (D / 2) + s * 8)
-          : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < QS; ++s) {
+      const u32x4 x = buf_load16(rs, qoff + hf * D + s * 16, 0);
+      qreg[qb][s] = qvalid ? x : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   // ---- softmax pieces
@@ -371,24 +405,35 @@ struct Core {
       }
     }
   }
-  // normalise and scatter query block qb back to raster order
-  __device__ __forceinline__ void finish(const Unit& u, int qb, int32_t qoff, bool qvalid) const {
+  // normalise and scatter query block qb back to raster order.  A lane
+  // holds 4 consecutive d of each 8-d group and its partner lane (32 apart)
+  // the other 4; one exchange per group pair gives each lane a whole group,
+  // so every store writes 16 bytes and the lane pair 32 contiguous bytes.
+  __device__ __forceinline__ void finish(const Unit& u, int qb, uint32_t qoff, bool qvalid) const {
     const float lp = l0[qb] + l1[qb];
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
                                                      false, false);
     const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-    if (qvalid) {
-      uint16_t* dst = p.out + u.base + qoff;
+    const Rsrc rs = make_rsrc(p.out + u.base);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hf;
-          const u32x2 w{pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv),
-                        pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + d) = w;
-        }
-    }
+      for (int g = 0; g < 4; g += 2) {
+        // a: this lane's 4 d of group g; b: of group g+1
+        const uint32_t a0 = pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv);
+        const uint32_t a1 = pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
+        const uint32_t b0 =
+            pack_bf16x2(acc[qb][db][4 * g + 4] * inv, acc[qb][db][4 * g + 5] * inv);
+        const uint32_t b1 =
+            pack_bf16x2(acc[qb][db][4 * g + 6] * inv, acc[qb][db][4 * g + 7] * inv);
+        // lanes 0-31 end with group g+1 (their own half first), lanes 32-63
+        // with group g (the partner's half first)
+        const auto x0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+        const u32x4 w{x0[0], x1[0], x0[1], x1[1]};
+        const int d = db * 32 + 8 * (g + 1 - hf);
+        if (qvalid) __builtin_amdgcn_raw_buffer_store_b128(w, rs, qoff + d * 2, 0, 0);
+      }
   }
 };
 
@@ -409,12 +454,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) attn_bf16_kernel(AttnP
 
   C c(p, smem);
   const Unit u = decode_unit(p, unit);
-  int32_t* tab = c.table();
+  uint32_t* tab = c.table();
   if (!FULL) {
     c.build_table(tab, u.win);
     __syncthreads();
   }
-  int32_t qoff[QB];
+  uint32_t qoff[QB];
   bool qvalid[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -502,6 +547,240 @@ __global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) attn_bf16_kernel(AttnP
 }
 
 
+// Barrier that orders LDS accesses only.  Global stores in flight (the output
+// of a finished unit) do not hold the workgroup up; loads whose registers feed
+// LDS stores are waited for by those stores' own register dependences, and
+// direct global-to-LDS loads by an explicit wait_vmem() before the barrier
+// that publishes them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Waits until every vector memory operation of this wave has completed
+// (vmcnt = 0; expcnt and lgkmcnt left at their maximum).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS of the persistent kernel: the tile buffers, two window tables (the
+// current unit's and the next one's) and, per wave, a staging area for the
+// next unit's Q rows, filled by direct global-to-LDS loads.
+template <int D, bool FULL, int NW, int KT>
+struct PersistLayout {
+  using TL = Tiles<D, NW, 1, KT>;
+  static constexpr int CPR = D / 8;        // 16B chunks per Q row
+  static constexpr int RPI = 64 / CPR;     // Q rows per load instruction (64 lanes x 16B)
+  static constexpr int QI = 32 / RPI;      // instructions per wave and unit
+  static constexpr int kQWave = 32 * D * 2;
+  __host__ __device__ static constexpr size_t table_bytes(int m) {
+    return FULL ? 0 : ((size_t)m * 4 + 15) / 16 * 16;
+  }
+  __host__ __device__ static constexpr size_t stage_offset(int m) {
+    return TL::tileBytes + 2 * table_bytes(m);
+  }
+  __host__ __device__ static constexpr size_t bytes(int m) {
+    return stage_offset(m) + (size_t)NW * kQWave;
+  }
+};
+
+// Persistent form of the unit kernel: one workgroup per CU; slot s of XCD x
+// runs units x*upx + s + j*S (S workgroups per XCD), j = 0..J-1, with the
+// unit kernel's tile loop.  The operands the next unit starts with are loaded
+// into registers the current unit no longer needs: its K tile 0 in the slot
+// of the current unit's tile nkt, its V tile 0 and K tile 1 in the slots of
+// tile nkt+1, and its Q rows once the current unit's last scores are formed.
+// The tile count is rounded up to an even number (a padding tile has only
+// masked keys), so tile t of every unit uses buffer t & 1.
+template <int D, bool FULL, int NW, int KT>
+__global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnParams p) {
+  using C = Core<D, FULL, NW, 1, KT>;
+  using TL = typename C::TL;
+  using PL = PersistLayout<D, FULL, NW, KT>;
+  constexpr int kKT = KT;
+  using Scores = typename C::Scores;
+  using Probs = typename C::Probs;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int S = gridDim.x >> 3;
+  const int ubeg = xcd * p.units_per_xcd;
+  const int uend = min(ubeg + p.units_per_xcd, p.units);
+  const int first = ubeg + slot;
+  if (first >= uend) return;                  // whole workgroup exits together
+  const int J = (uend - first + S - 1) / S;   // units of this workgroup
+
+  C c(p, smem);
+  // even tile count; a padding tile holds only keys >= L, which the mask removes
+  const int nkt = (c.nkt + 1) & ~1;
+  if (nkt != c.nkt) c.tmask = min(c.tmask, c.nkt);
+  unsigned char* tables = smem + TL::tileBytes;
+  auto tab_of = [&](int j) __attribute__((always_inline)) {
+    return reinterpret_cast<uint32_t*>(tables + (j & 1) * PL::table_bytes(c.m));
+  };
+  auto unit_at = [&](int j) __attribute__((always_inline)) {
+    return decode_unit(p, first + min(j, J - 1) * S);
+  };
+  // Q rows of unit u; and its output rows, both addressed through its table
+  auto load_q_of = [&](const Unit& u, const uint32_t* tb) __attribute__((always_inline)) {
+    const int r = c.qrow(u, 0);
+    const bool valid = r < c.m;
+    c.load_q(u, 0, valid ? c.tok(tb, r) : 0u, valid);
+  };
+  // This wave's staged Q rows: 16B chunk ch of row r at position ch ^ (r %
+  // CPR), so the 32 lanes reading one chunk of 32 rows hit distinct banks.
+  const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  unsigned char* qstage = smem + PL::stage_offset(c.m) + wave * PL::kQWave;
+  // instruction i of PL::QI: 64 lanes x 16B to qstage + 1024*i + 16*lane
+  auto stage_q = [&](const Unit& u, const uint32_t* tb, int i) __attribute__((always_inline)) {
+    const int lane = c.tid & 63;
+    const int r = PL::RPI * i + lane / PL::CPR;
+    const int ch = (lane % PL::CPR) ^ (r % PL::CPR);
+    const int row = min(u.qt * TL::kQT + wave * 32 + r, c.m - 1);
+    const char* src = reinterpret_cast<const char*>(p.q + u.base) + c.tok(tb, row) + ch * 16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                      (__attribute__((address_space(3))) void*)(qstage + i * 1024),
+                                      16, 0, 0);
+  };
+  auto unstage_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) {
+      const int ch = c.hf * (PL::CPR / 2) + s;
+      c.qreg[0][s] = *reinterpret_cast<const u32x4*>(
+          qstage + (c.l32 * PL::CPR + (ch ^ (c.l32 % PL::CPR))) * 16);
+    }
+  };
+  auto finish_of = [&](const Unit& u, const uint32_t* tb) __attribute__((always_inline)) {
+    const int r = c.qrow(u, 0);
+    const bool valid = r < c.m;
+    c.finish(u, 0, valid ? c.tok(tb, r) : 0u, valid);
+  };
+
+  // ---- unit 0: tables of units 0 and 1; its operands from global memory
+  Unit uc = unit_at(0);
+  Unit un = unit_at(1);
+  if (!FULL) {
+    c.build_table(tab_of(0), uc.win);
+    if (J > 1) c.build_table(tab_of(1), un.win);
+    lds_barrier();
+  }
+  load_q_of(uc, tab_of(0));
+  {
+    u32x4 k1[TL::KPASS];
+    c.load_k(uc, tab_of(0), 0);
+    c.load_v(uc, tab_of(0), 0);
+    c.load_k_to(k1, uc, tab_of(0), 1);
+    c.store_k(0);
+    c.store_v(0);
+    c.store_k_from(k1, 1);
+  }
+  lds_barrier();  // tiles 0 and 1 of unit 0 are in LDS
+  Scores sA, sB;
+  c.compute_s(c.sK(0), sA);
+  auto copy = [&](Scores& dst, const Scores& src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) dst[0][kb] = src[0][kb];
+  };
+  const int t1 = min(nkt, c.tmask);  // iterations t < t1 - 1 need no mask on S(t+1)
+  const int qstep = nkt - 2;         // staging load i of the next unit's Q goes out in
+                                     // iteration i mod qstep (never in the last one)
+
+  // Unit j starts with S(0) in sA, its tile 0 in K buffer 0, tile 1 in K
+  // buffer 1 and V tile 0 in V buffer 0.
+  for (int j = 0; j < J; ++j) {
+    c.redefine_lane_ids();
+    const bool has_next = j + 1 < J;
+    const uint32_t* tab = tab_of(j);
+    const uint32_t* tabn = tab_of(j + 1);
+    c.reset();
+    {
+      float mx[1];
+      if (c.tmask == 0) c.mask_s(sA, 0);
+      c.rowmax_all(sA, mx);
+      c.update_max(mx);
+    }
+    c.load_v(uc, tab, 1);
+    c.load_k(uc, tab, 2);
+    // Every wave is done with K(0) (and with the previous unit's output
+    // rows, read through its table) before iteration 0 refills the buffer
+    // and the next unit's table overwrites the previous unit's.
+    lds_barrier();
+    if (!FULL && j >= 1 && has_next) c.build_table(tab_of(j + 1), un.win);
+
+    // Iteration t: as in the unit kernel; the loads past the unit's last tile
+    // bring the next unit's first tiles.
+    auto iter = [&](int t, Scores& sc, Scores& sn, auto masked) __attribute__((always_inline)) {
+      Probs pb;
+      float mxn[1];
+      c.compute_s(c.sK((t + 1) & 1), sn);
+      c.make_p(sc, pb);
+      c.pv(c.sV(t & 1), pb);
+      if constexpr (decltype(masked)::value) c.mask_s(sn, (t + 1) * kKT);
+      c.rowmax_all(sn, mxn);
+      c.store_v((t + 1) & 1);
+      c.store_k(t & 1);
+      lds_barrier();
+      const int tv = t + 2, tk = t + 3;
+      if (tv < nkt || (has_next && tv == nkt)) {
+        const bool cur = tv < nkt;
+        const Unit u = cur ? uc : un;  // by value: the choice stays in registers
+        c.load_v(u, cur ? tab : tabn, cur ? tv : 0);
+      }
+      if (tk < nkt || (has_next && tk <= nkt + 1)) {
+        const bool cur = tk < nkt;
+        const Unit u = cur ? uc : un;
+        c.load_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
+      }
+      if (has_next && t < qstep)
+        for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
+      c.update_max(mxn);
+    };
+    int t = 0;
+    for (; t + 2 < t1; t += 2) {
+      iter(t, sA, sB, bool_c<false>{});
+      iter(t + 1, sB, sA, bool_c<false>{});
+    }
+    if (t + 1 < t1) {
+      iter(t, sA, sB, bool_c<false>{});
+      ++t;
+      copy(sA, sB);
+    }
+    for (; t + 2 < nkt; t += 2) {
+      iter(t, sA, sB, bool_c<true>{});
+      iter(t + 1, sB, sA, bool_c<true>{});
+    }
+    if (t + 1 < nkt) {
+      iter(t, sA, sB, bool_c<true>{});
+      ++t;
+      copy(sA, sB);
+    }
+    {
+      Probs pb;
+      c.make_p(sA, pb);
+      c.pv(c.sV(t & 1), pb);
+    }
+    if (!has_next) {
+      finish_of(uc, tab);
+      break;
+    }
+    // The next unit's K tile 0 is in buffer 0 (stored by iteration nkt-2).
+    // Its V tile 0 and K tile 1 go to buffers whose last readers (the P V
+    // product of tile nkt-2, the scores of tile nkt-1) ran before the last
+    // barrier.  Its Q rows come from this wave's staging area (each wave
+    // stages and reads only its own rows).  Its first scores are formed
+    // before this unit's output stores are issued, so no wait for a load
+    // covers those stores.
+    wait_vmem();
+    unstage_q();
+    c.store_v(0);
+    c.store_k(1);
+    c.compute_s(c.sK(0), sA);
+    finish_of(uc, tab);
+    uc = un;
+    un = unit_at(j + 2);
+  }
+}
+
 // Workgroup shape: NW waves of QB query blocks (32 rows each).
 #ifndef BASA_ATTN_WAVES
 #define BASA_ATTN_WAVES 8
@@ -511,6 +790,13 @@ __global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) attn_bf16_kernel(AttnP
 #endif
 #ifndef BASA_ATTN_KTILE
 #define BASA_ATTN_KTILE 64
+#endif
+// Persistent kernel on/off and its key-tile size.
+#ifndef BASA_PERSISTENT
+#define BASA_PERSISTENT 1
+#endif
+#ifndef BASA_PERSISTENT_KTILE
+#define BASA_PERSISTENT_KTILE 64
 #endif
 template <typename K>
 int set_lds_limit(K kernel, bool& done) {
@@ -522,15 +808,55 @@ int set_lds_limit(K kernel, bool& done) {
   return BASA_OK;
 }
 
-template <int D, bool FULL, int NW, int QB, int KT>
-int launch(const AttnParams& p0, hipStream_t stream) {
-  using TL = Tiles<D, NW, QB, KT>;
-  AttnParams p = p0;
-  p.nQT = (p.m + TL::kQT - 1) / TL::kQT;
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cache[dev] = v;  // benign race: every thread stores the same value
+  }
+  return cache[dev];
+}
+
+// Fills in the unit count of a launch with kQT query rows per unit.
+inline int set_units(AttnParams& p, int kQT) {
+  p.nQT = (p.m + kQT - 1) / kQT;
   const int64_t units = (int64_t)p.batch_heads * p.nW * p.nQT;
   if (units > (int64_t)INT32_MAX / 2) return BASA_ERR_UNSUPPORTED;
   p.units = (int32_t)units;
   p.units_per_xcd = (p.units + 7) / 8;
+  return BASA_OK;
+}
+
+// Persistent kernel when the units are long enough and its LDS fits; returns
+// -1 (nothing launched) otherwise.
+template <int D, bool FULL, int NW, int KT>
+int launch_persistent(const AttnParams& p0, hipStream_t stream) {
+  using TL = Tiles<D, NW, 1, KT>;
+  using SL = PersistLayout<D, FULL, NW, KT>;
+  const int nkt = (p0.m + p0.G + KT - 1) / KT;
+  const size_t lds = SL::bytes(p0.m);
+  if (nkt < kPersistentMinTiles || lds > 160 * 1024) return -1;
+  AttnParams p = p0;
+  if (int e = set_units(p, TL::kQT)) return e;
+  static bool attr = false;
+  if (set_lds_limit(&attn_bf16_persistent_kernel<D, FULL, NW, KT>, attr)) return BASA_ERR_HIP;
+  const int per_xcd = max(1, min(p.units_per_xcd, cu_count() / 8));
+  hipLaunchKernelGGL((attn_bf16_persistent_kernel<D, FULL, NW, KT>), dim3((unsigned)(8 * per_xcd)),
+                     dim3(TL::kThreads), lds, stream, p);
+  return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
+template <int D, bool FULL, int NW, int QB, int KT>
+int launch_unit(const AttnParams& p0, hipStream_t stream) {
+  using TL = Tiles<D, NW, QB, KT>;
+  AttnParams p = p0;
+  if (int e = set_units(p, TL::kQT)) return e;
   const size_t lds = TL::tileBytes + (FULL ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
   static bool attr = false;
@@ -540,12 +866,22 @@ int launch(const AttnParams& p0, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
-template <int D>
-int launch_d(const AttnParams& p, bool full, hipStream_t stream) {
+template <int D, bool FULL>
+int launch_full_or_window(const AttnParams& p, hipStream_t stream) {
   // a head dim of 64 needs 64-key tiles to give every thread of 8 waves work
   constexpr int KT = (D == 64 && BASA_ATTN_KTILE * D < 64 * 64) ? 64 : BASA_ATTN_KTILE;
-  return full ? launch<D, true, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream)
-              : launch<D, false, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream);
+  constexpr int KTS = (D == 64 && BASA_PERSISTENT_KTILE * D < 64 * 64) ? 64 : BASA_PERSISTENT_KTILE;
+#if BASA_PERSISTENT
+  const int e = launch_persistent<D, FULL, BASA_ATTN_WAVES, KTS>(p, stream);
+  if (e >= 0) return e;
+#endif
+  return launch_unit<D, FULL, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream);
+}
+
+template <int D>
+int launch_d(const AttnParams& p, bool full, hipStream_t stream) {
+  return full ? launch_full_or_window<D, true>(p, stream)
+              : launch_full_or_window<D, false>(p, stream);
 }
 
 }  // namespace
