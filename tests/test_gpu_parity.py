@@ -180,6 +180,58 @@ def test_ultra_sampled():
     _sampled_check(wl, shift, heads=[5, 19], windows=sample_windows(wl.n_windows, 3))
 
 
+# ------------------------------------------------------ launch configurations
+# Shapes chosen to drive each path of the bf16 launcher: the persistent kernel
+# with several units per workgroup (including the fewest tiles it takes, a
+# ragged unit count per XCD, an odd tile count padded with a masked tile, the
+# memory-bias masked phase, head dim 64, the BNHD layout with B > 1), and the
+# per-unit kernel for units of fewer than four tiles and for windows whose
+# tables do not fit next to the persistent kernel's buffers.
+PATHS = [
+    # name, B, H, D, grid, window, pool, shift, mem_bias, layout
+    ("min tiles, ragged units", 2, 37, 128, (48, 80), (16, 16), None, (8, 3), 0.0, "bhnd"),
+    ("odd tiles + bias phase", 1, 64, 128, (40, 40), (20, 20), (8, 8), (10, 7), math.log(64.0), "bhnd"),
+    ("head dim 64", 1, 80, 64, (32, 64), (16, 16), (8, 8), (5, 11), 0.0, "bhnd"),
+    ("bnhd, batch 2", 2, 80, 128, (32, 32), (16, 16), (8, 8), (8, 8), 0.0, "bnhd"),
+    ("short units", 1, 8, 128, (64, 64), (8, 8), (8, 8), (4, 4), 0.0, "bhnd"),
+    ("window of 4096", 1, 2, 128, (64, 64), (64, 64), (16, 16), (31, 40), 0.0, "bhnd"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PATHS)))
+def test_launch_paths(case):
+    name, B, H, D, grid, window, pool, shift, bias, layout = PATHS[case]
+    n = int(np.prod(grid))
+    log(f"path '{name}': B={B} H={H} D={D} grid={grid} window={window} pool={pool}")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=300 + case)
+    km = vm = None
+    if pool is not None:
+        km, vm = O.pool_mean(k, grid, pool), O.pool_mean(v, grid, pool)
+    ref = O.window_attention(q, k, v, grid, window, shift, km, vm, mem_logit_bias=bias)
+    conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)
+    qg, kg, vg = (to_gpu(conv(x), "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool, layout=layout) if pool is not None else None
+    out = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem, mem_bias=bias, layout=layout)
+    _sync()
+    got = to_np(out)
+    if layout == "bnhd":
+        got = got.transpose(0, 2, 1, 3)
+    assert_close(got, ref, "bf16", f"path {name}")
+
+
+def test_full_attn_many_units():
+    B, H, n, D = 1, 48, 2048, 128     # 384 units: several per workgroup
+    log("full attention, several units per workgroup")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=21)
+    out = S.full_attn(to_gpu(q, "bf16"), to_gpu(k, "bf16"), to_gpu(v, "bf16"))
+    _sync()
+    rows = np.unique(np.linspace(0, n - 1, 96).astype(np.int64))
+    heads = [0, 17, 31, 47]
+    got = to_np(out)[:, heads][:, :, rows]
+    ref = O.full_attention(q[:, heads], k[:, heads], v[:, heads], rows=rows)
+    assert_close(got, ref, "bf16", "full many units")
+
+
 # ------------------------------------------------------------- dense kernel
 @pytest.mark.parametrize("dtype,n,D", [("bf16", 4096, 128), ("bf16", 1000, 128),
                                        ("bf16", 777, 64), ("f32", 300, 64), ("f32", 520, 128)])
