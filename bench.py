@@ -265,7 +265,7 @@ def cpu_baseline(wl, target_s):
     cache = {}
     calls, heads_done, flops, t_total = 0, 0, 0, 0.0
     # whole heads, cycling through the schedule phases, until ~target_s
-    while t_total < target_s and heads_done < 4 * wl.heads:
+    while t_total < target_s and heads_done < 32 * wl.heads:
         h, block = heads_done % wl.heads, heads_done // wl.heads
         if h not in cache:
             cache[h] = tuple(W.head_values(wl, t, h) for t in range(3))
@@ -396,7 +396,7 @@ def main():
         roof = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "attn_bf16_kernel<128,false>"
+    roof["kernel"] = "attn_bf16_persistent_kernel<128,false,8,64>"
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = byts
     roof["mfma_frac"] = res["window_attn_mfma_frac"]
