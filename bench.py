@@ -288,6 +288,77 @@ def cpu_baseline(wl, target_s):
             "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
 
 
+def window_permutation(grid, window, shift, device):
+    """Raster index of every token in window-major order under the shifted
+    partition: windows in raster order of the window grid, tokens in raster
+    order inside each window, for the grid rolled by -shift.  One
+    ``index_select`` with it materialises the roll and the partition (the
+    copies a stock-backend deployment makes); its inverse undoes both."""
+    import torch
+    g, w, s = list(grid), list(window), list(shift)
+    if len(g) == 2:
+        g, w, s = [1] + g, [1] + w, [0] + s
+    idx = torch.arange(g[0] * g[1] * g[2], dtype=torch.int64).view(*g)
+    idx = torch.roll(idx, shifts=[-x for x in s], dims=(0, 1, 2))
+    idx = idx.view(g[0] // w[0], w[0], g[1] // w[1], w[1], g[2] // w[2], w[2])
+    perm = idx.permute(0, 2, 4, 1, 3, 5).reshape(-1)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel(), dtype=torch.int64)
+    return perm.to(device), inv.to(device)
+
+
+def compose_attention(S, q, k, v, mem, grid, window, shift, perms=None):
+    """The composition a stock backend runs: materialised roll + partition of
+    Q, K, V; attention over the window-contiguous tensors (the library kernel
+    with the identity address map: a grid of nW rows of m tokens, one window
+    per row, the pooled memory shared); then unpartition + unroll of O."""
+    perm, inv = perms or window_permutation(grid, window, shift, q.device)
+    n = q.shape[2]
+    m = int(math.prod(window))
+    qw, kw, vw = (x.index_select(2, perm) for x in (q, k, v))
+    ow = S.window_attn(qw, kw, vw, (n // m, m), (1, m), (0, 0), mem=mem)
+    return ow.index_select(2, inv)
+
+
+def measure_composition(S, wl, sets, steps, stream):
+    """Times the composition baseline beside the fused kernel (events per
+    part); the memory broadcast a stock kernel would also need (every window's
+    copy of the pooled memory) is timed on its own."""
+    import torch
+    B, H, n, D, G = wl.batch, wl.heads, wl.n_tokens, wl.head_dim, wl.mem_tokens
+    nW, m = wl.n_windows, wl.window_tokens
+    shifts = [S.shift_for_block(i, wl.schedule, wl.window) for i in range(4)]
+    perms = [window_permutation(wl.grid, wl.window, sh, sets[0][0].device) for sh in shifts]
+    mems = [S.pool_kv(k, v, wl.grid, wl.pool) for (q, k, v) in sets]
+    parts = {"gather": [], "attention": [], "scatter": [], "broadcast": []}
+    for i in range(steps + 2):
+        q, k, v = sets[i % len(sets)]
+        mem = mems[i % len(sets)]
+        perm, inv = perms[i % 4]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        qw, kw, vw = (x.index_select(2, perm) for x in (q, k, v))
+        ev[1].record(stream)
+        ow = S.window_attn(qw, kw, vw, (nW, m), (1, m), (0, 0), mem=mem)
+        ev[2].record(stream)
+        ow.index_select(2, inv)
+        ev[3].record(stream)
+        mem[0].unsqueeze(2).expand(B, H, nW, G, D).contiguous()
+        mem[1].unsqueeze(2).expand(B, H, nW, G, D).contiguous()
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            for j, key in enumerate(parts):
+                parts[key].append(ev[j].elapsed_time(ev[j + 1]))
+    r = {key: sum(x) / len(x) for key, x in parts.items()}
+    r["total_without_broadcast"] = r["gather"] + r["attention"] + r["scatter"]
+    r["total_with_broadcast"] = r["total_without_broadcast"] + r["broadcast"]
+    r["note"] = ("materialised roll+partition (index_select), attention over the "
+                 "window-contiguous tensors, unpartition+unroll; broadcast = every window's "
+                 "copy of the pooled K/V memory that a stock dense kernel also needs")
+    return r
+
+
 def measure_window(S, wl, args, stream, dev, with_dense=True):
     n, m, G, D, H, B = (wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.heads,
                        wl.batch)
@@ -380,6 +451,14 @@ def main():
     print(f"[bench] {head.name}: attn {res['window_attn_ms']['mean']*1e3:.1f} us "
           f"({res['window_attn_tflops']:.0f} TFLOP/s), pool {res['pool_kv_ms']['mean']*1e3:.1f} us",
           file=sys.stderr, flush=True)
+    comp_sets = make_sets(head, args.sets, dev)
+    comp = measure_composition(S, head, comp_sets, max(10, args.steps // 2), stream)
+    del comp_sets
+    comp["fused_attention_ms"] = res["window_attn_ms"]["mean"]
+    comp["composition_over_fused"] = comp["total_with_broadcast"] / res["window_attn_ms"]["mean"]
+    print(f"[bench] composition baseline: gather {comp['gather']*1e3:.1f} + attention "
+          f"{comp['attention']*1e3:.1f} + scatter {comp['scatter']*1e3:.1f} + broadcast "
+          f"{comp['broadcast']*1e3:.1f} us", file=sys.stderr, flush=True)
     res_o = measure_window(S, other, args, stream, dev)
     print(f"[bench] {other.name}: attn {res_o['window_attn_ms']['mean']*1e3:.1f} us "
           f"({res_o['window_attn_tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
@@ -427,6 +506,7 @@ def main():
         "roofline": roof,
         "ms_per_attn_call": res["window_attn_ms"]["mean"],
         "windows": {f"{res['m']}": res, f"{res_o['m']}": res_o},
+        "composition_baseline": comp,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
