@@ -9,3 +9,6 @@ from .basa_oracle import (  # noqa: F401
     masked_attention_bruteforce, mem_tokens, pool_mean, shift_for_block,
     theoretical_speedup, window_attention, window_attention_head, window_flops,
     window_id, window_token_index)
+from .basa_backward import (  # noqa: F401
+    attention_backward_rows, pool_backward, window_attention_backward,
+    window_attention_backward_head)
