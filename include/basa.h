@@ -151,6 +151,68 @@ int basa_window_attn(const void* q, const void* k, const void* v,
                      int32_t dtype, int32_t layout, void* stream);
 
 /*
+ * basa_window_attn that also writes, for every query token, the natural-log
+ * log-sum-exp of its scaled and biased logits over [window keys; memory
+ * keys] -- the statistic the backward recomputes the softmax from.  The
+ * training side of the method (the dense-teacher adaptation the BASA pages
+ * describe) needs gradients; this forward feeds basa_window_attn_bwd.
+ *   lse   device fp32 [B, H, n] (n = prod(grid), tokens in raster order),
+ *         4-byte aligned, not overlapping any other argument
+ * Other arguments and errors as basa_window_attn; UNSUPPORTED unless dtype
+ * is BASA_BF16.
+ */
+int basa_window_attn_fwd(const void* q, const void* k, const void* v,
+                         const void* k_mem, const void* v_mem, int64_t n_mem,
+                         void* out, float* lse,
+                         int32_t batch, int32_t heads, int32_t head_dim,
+                         int32_t ndim, const int32_t* grid, const int32_t* window,
+                         const int32_t* shift, float scale, float mem_bias,
+                         int32_t dtype, int32_t layout, void* stream);
+
+/*
+ * Bytes of device workspace basa_window_attn_bwd needs for this shape (pool
+ * NULL: no memory).  Returns -1 for arguments it rejects.  Host only.
+ */
+int64_t basa_window_attn_bwd_workspace(int32_t batch, int32_t heads, int32_t head_dim,
+                                       int32_t ndim, const int32_t* grid,
+                                       const int32_t* pool);
+
+/*
+ * Gradients of basa_window_attn with respect to q, k and v [BASA-1, "The
+ * BASA Method"; BASA-2 four-parts paragraph; SFA shared softmax], the
+ * memory included: k_mem and v_mem must be the mean pool of k and v over
+ * `pool` (basa_pool_kv), and their gradient flows back into dk and dv (each
+ * token of a cell receives the cell's gradient divided by the cell size).
+ * Softmax probabilities are recomputed from lse.
+ *   q, k, v          device, B x H x n x D in `layout` (the forward's inputs)
+ *   k_mem, v_mem     device [B, H, G, D]: the forward's memory, or NULL with
+ *                    pool NULL for attention without memory
+ *   out, dout        device, B x H x n x D in `layout`: forward output and
+ *                    the gradient of the loss with respect to it
+ *   lse              device fp32 [B, H, n] from basa_window_attn_fwd
+ *   dq, dk, dv       device, B x H x n x D in `layout`: written entirely
+ *   workspace        device, at least basa_window_attn_bwd_workspace()
+ *                    bytes, 16-byte aligned; contents are scratch
+ *   grid, window, shift, scale, mem_bias as for the forward; pool as for
+ *   basa_pool_kv (NULL: no memory)
+ * bf16 only; fp32 accumulation; P and dS are rounded to bf16 as MFMA
+ * operands.  Errors: INVALID_ARG (NULL, bad dims, non-dividing window or
+ * pool, pool/k_mem/v_mem not all given or all NULL, workspace too small,
+ * an output overlapping an input, another output or the workspace),
+ * UNSUPPORTED (dtype, head_dim, window too large).
+ */
+int basa_window_attn_bwd(const void* q, const void* k, const void* v,
+                         const void* k_mem, const void* v_mem,
+                         const void* out, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, int64_t workspace_bytes,
+                         int32_t batch, int32_t heads, int32_t head_dim,
+                         int32_t ndim, const int32_t* grid, const int32_t* window,
+                         const int32_t* shift, const int32_t* pool,
+                         float scale, float mem_bias,
+                         int32_t dtype, int32_t layout, void* stream);
+
+/*
  * Dense full attention out = softmax(scale * q k^T) v over all n_tokens keys
  * per (batch, head) [BASA-2 complexity paragraph: the O(n^2) cost that window
  * attention reduces to O(n*m)].  Built only to measure realised against

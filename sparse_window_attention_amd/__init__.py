@@ -18,7 +18,7 @@ __all__ = [
     "BASA_F32", "BASA_BF16", "BASA_LAYOUT_BHND", "BASA_LAYOUT_BNHD",
     "SCHED_NONE", "SCHED_ALTERNATE", "SCHED_FOUR_PHASE", "BasaError", "lib",
     "library_path", "version", "mem_tokens", "shift_for_block", "pool_kv",
-    "window_attn", "full_attn",
+    "window_attn", "window_attn_fwd", "window_attn_bwd", "bwd_workspace_bytes", "full_attn",
 ]
 
 BASA_OK, BASA_ERR_INVALID_ARG, BASA_ERR_UNSUPPORTED, BASA_ERR_HIP = 0, 1, 2, 3
@@ -65,6 +65,12 @@ def _load() -> ctypes.CDLL:
                                             i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
         "basa_full_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i64, i32, f32, i32,
                                           i32, vp]),
+        "basa_window_attn_fwd": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32,
+                                                i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
+        "basa_window_attn_bwd_workspace": (i64, [i32, i32, i32, i32, pi32, pi32]),
+        "basa_window_attn_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                i64, i32, i32, i32, i32, pi32, pi32, pi32, pi32,
+                                                f32, f32, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -208,6 +214,95 @@ def window_attn(q, k, v, grid: Sequence[int], window: Sequence[int], shift: Sequ
                                 _arr(shift), s, float(mem_bias), _dtype_code(q), lay,
                                 _stream(q)))
     return out
+
+
+def _mem_args(q, mem, B, H, D):
+    if mem is None:
+        return None, None, 0
+    km, vm = mem
+    _check_tensors(q, km, vm)
+    if km.dim() != 4 or tuple(km.shape[:2]) != (B, H) or km.shape[3] != D \
+            or tuple(vm.shape) != tuple(km.shape):
+        raise ValueError("memory tensors must be [B, H, G, D]")
+    return km.data_ptr(), vm.data_ptr(), km.shape[2]
+
+
+def window_attn_fwd(q, k, v, grid: Sequence[int], window: Sequence[int], shift: Sequence[int],
+                    mem: Optional[tuple] = None, scale: Optional[float] = None,
+                    mem_bias: float = 0.0, out=None, lse=None, layout: str = "bhnd"):
+    """window_attn that also returns the per-query log-sum-exp (fp32 [B, H, n])
+    the backward needs: returns (out, lse)."""
+    torch = _torch()
+    _check_tensors(q, k, v)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v shapes differ")
+    if n != math.prod(grid):
+        raise ValueError("token count does not match the grid")
+    out = torch.empty_like(q) if out is None else out
+    _check_tensors(q, out)
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+    km_p, vm_p, G = _mem_args(q, mem, B, H, D)
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_window_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, G,
+                                    out.data_ptr(), lse.data_ptr(), B, H, D, len(grid),
+                                    _arr(grid), _arr(window), _arr(shift), s, float(mem_bias),
+                                    _dtype_code(q), lay, _stream(q)))
+    return out, lse
+
+
+def bwd_workspace_bytes(batch: int, heads: int, head_dim: int, grid: Sequence[int],
+                        pool: Optional[Sequence[int]] = None) -> int:
+    b = lib.basa_window_attn_bwd_workspace(int(batch), int(heads), int(head_dim), len(grid),
+                                           _arr(grid), None if pool is None else _arr(pool))
+    if b < 0:
+        raise BasaError(BASA_ERR_INVALID_ARG, "invalid shape for the backward workspace")
+    return int(b)
+
+
+def window_attn_bwd(q, k, v, out, dout, lse, grid: Sequence[int], window: Sequence[int],
+                    shift: Sequence[int], mem: Optional[tuple] = None,
+                    pool: Optional[Sequence[int]] = None, scale: Optional[float] = None,
+                    mem_bias: float = 0.0, grads: Optional[tuple] = None, workspace=None,
+                    layout: str = "bhnd"):
+    """Gradients (dq, dk, dv) of window_attn; with memory, ``mem`` must be
+    pool_kv(k, v, grid, pool) and its gradient is folded into dk and dv."""
+    torch = _torch()
+    _check_tensors(q, k, v, out, dout)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    for t in (k, v, out, dout):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError("q, k, v, out, dout shapes differ")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on q's device")
+    if (mem is None) != (pool is None):
+        raise ValueError("mem and pool go together")
+    km_p, vm_p, _ = _mem_args(q, mem, B, H, D)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = grads
+    _check_tensors(q, dq, dk, dv)
+    need = bwd_workspace_bytes(B, H, D, grid, pool)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_window_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), B, H, D, len(grid), _arr(grid),
+        _arr(window), _arr(shift), None if pool is None else _arr(pool), s, float(mem_bias),
+        _dtype_code(q), lay, _stream(q)))
+    return dq, dk, dv
 
 
 def full_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "bhnd"):

@@ -66,28 +66,8 @@ struct Tiles {
                 "V tile must split evenly over the threads");
 };
 
-// Slot of key `key` (0..KT-1) in the transposed V tile: within each group of
-// 16 keys, the order matches how the S^T accumulator registers map onto the
-// k index of the P V product's operand.
-__device__ __forceinline__ int vslot(int key) {
-  const int a = key >> 2, i = key & 3;
-  return (a >> 2) * 16 + (a & 1) * 8 + ((a >> 1) & 1) * 4 + i;
-}
-
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
-
-// Raw buffer resource over a (batch, head) slice: wave-uniform base in
-// scalar registers, per-lane 32-bit byte offsets (every offset inside a slice
-// is below 2^32 bytes, checked on the host).
-using Rsrc = __amdgpu_buffer_rsrc_t;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFFu,
-                                           0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
 
 // One work unit: element offset of its (batch, head) slice in Q/K/V/O, its
 // (batch, head) index, window and query tile.
@@ -413,7 +393,13 @@ struct Core {
     const float lp = l0[qb] + l1[qb];
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
                                                      false, false);
-    const float inv = 1.0f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+    const float lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float inv = 1.0f / lsum;
+    if (p.lse != nullptr && qvalid && hf == 0) {
+      // natural-log log-sum-exp of the scaled, biased logits of this query
+      const uint32_t token = qoff / stb;
+      p.lse[(int64_t)u.bh * p.n_tok + token] = (m_used[qb] + __builtin_log2f(lsum)) * 0.6931471805599453f;
+    }
     const Rsrc rs = make_rsrc(p.out + u.base);
 #pragma unroll
     for (int db = 0; db < DB; ++db)

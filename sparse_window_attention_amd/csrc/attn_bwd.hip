@@ -1,0 +1,552 @@
+// Backward of shifted-window attention with pooled K/V memory (bf16, gfx950).
+//
+// The forward (BASA forum summary, "The BASA Method": attention inside
+// shifted windows; BASA discussion reply, the four parts of the method: a
+// global memory of pooled K/V appended to every window's keys under one
+// softmax) is differentiated exactly.  Per window, with S = scale Q Kc^T +
+// bias over Kc = [window keys; memory keys], P = softmax(S), O = P Vc:
+//   Dv_i  = sum_d dO_id O_id
+//   dS    = P * (dO Vc^T - Dv)
+//   dQ    = scale dS Kc,   dKc = scale dS^T Q,   dVc = P^T dO
+// P is recomputed from the forward's log-sum-exp.  A window key belongs to
+// one window; a memory key collects the gradient of every query of its
+// (batch, head), which mean pooling hands on to each token of its cell
+// divided by the cell size.
+//
+// Kernels (one workgroup of 8 waves per unit, XCD-aware unit order):
+//   dvec     Dv for every token
+//   dq       query-stationary: 256 queries of a window against the key
+//            sequence [window keys; memory keys] in tiles of 32 keys:
+//            S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//   dkdv     key-stationary: 256 keys (32 per wave) against blocks of 32
+//            queries: S = Q K^T, P; pass 0: dV^T += dO^T P; pass 1:
+//            dP = dO V^T, dS, dK^T += Q^T dS.  Memory-key units cover one
+//            chunk of the head's queries each and write fp32 partial sums;
+//            window-key units write the final dK, dV of their tokens, adding
+//            the pooled memory gradient of the token's cell.
+//   memsum   sums the memory partials and divides by the cell size
+// All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
+// rounded to bf16 as operands.  Transposed LDS tiles order their k index the
+// way the S accumulators hold it (vslot), as in the forward's V^T.
+#include "basa_common.h"
+#include "basa_internal.h"
+
+namespace basa {
+
+namespace {
+
+constexpr int kNW = 8;                 // waves per workgroup
+constexpr int kThreads = kNW * 64;
+constexpr int kBlk = 32;               // keys per dq tile, queries per dkdv block
+constexpr int kUnit = kNW * 32;        // queries per dq unit, keys per dkdv unit
+
+template <int D>
+struct BT {
+  static constexpr int KS = D + 8;              // row-major tile stride (bf16)
+  static constexpr int TS = kBlk + 8;           // transposed tile stride (bf16)
+  static constexpr int kRow = kBlk * KS * 2;    // bytes of a 32-row tile
+  static constexpr int kTr = D * TS * 2;        // bytes of a transposed tile
+  static constexpr int CPR = D / 8;             // 16B chunks per row
+  static constexpr int QS = D / 16;             // MFMA steps over the head dim
+  static constexpr int DB = D / 32;             // 32-row blocks of a head-dim accumulator
+};
+
+__device__ __forceinline__ int64_t slice_base(const BwdParams& p, int bh) {
+  const int b = bh / p.heads, h = bh - b * p.heads;
+  return (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
+}
+
+// Unit of this workgroup with consecutive units on one XCD; -1 past the end.
+__device__ __forceinline__ int xcd_unit(int units) {
+  const int upx = (units + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  const int u = (blockIdx.x & 7) * upx + slot;
+  return (slot < upx && u < units) ? u : -1;
+}
+
+// Register r of an S accumulator holds row 8*(r/4) + 4*hf + r%4 of the tile.
+__device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Position of row i (0..31) in a per-lane-half permuted array of 32 floats:
+// lane half hf reads its 16 rows (in register order) at hf*16.
+__device__ __forceinline__ int perm32(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
+
+// Transposed store of one 16B row chunk: 8 values of row `row`, columns
+// (head dim) c8 .. c8+7, into tile [D][TS] at column slot vslot(row).
+template <int TS>
+__device__ __forceinline__ void store_tr(uint16_t* st, int row, int c8, const u32x4& x) {
+  const int slot = vslot(row);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    st[(c8 + 2 * e) * TS + slot] = (uint16_t)(x[e] & 0xffffu);
+    st[(c8 + 2 * e + 1) * TS + slot] = (uint16_t)(x[e] >> 16);
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Writes a head-dim accumulator (lane = row of the output, registers = 4
+// consecutive d of each 8-d group) as bf16 rows of 16 bytes per lane after a
+// lane-pair exchange.  `add` (fp32 [D] per row, may be null) is added first.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[BT<D>::DB], float mul,
+                                           const float* add, uint16_t* dst_slice, uint32_t off,
+                                           bool valid, int hf) {
+  const Rsrc rs = make_rsrc(dst_slice);
+#pragma unroll
+  for (int db = 0; db < BT<D>::DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; g += 2) {
+      float a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = acc[db][4 * g + i] * mul;
+      if (add != nullptr && valid) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(add + db * 32 + 8 * g + 4 * hf);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(add + db * 32 + 8 * (g + 1) + 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] += x0[i];
+          a[4 + i] += x1[i];
+        }
+      }
+      const uint32_t a0 = pack_bf16x2(a[0], a[1]), a1 = pack_bf16x2(a[2], a[3]);
+      const uint32_t b0 = pack_bf16x2(a[4], a[5]), b1 = pack_bf16x2(a[6], a[7]);
+      // lanes 0-31 end with group g+1 (own half first), lanes 32-63 with group g
+      const auto x0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+      const auto x1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+      const u32x4 w{x0[0], x1[0], x0[1], x1[1]};
+      const int d = db * 32 + 8 * (g + 1 - hf);
+      if (valid) __builtin_amdgcn_raw_buffer_store_b128(w, rs, off + d * 2, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------- dvec
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dvec_kernel(BwdParams p) {
+  constexpr int CPR = D / 8, RPW = 64 / CPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / CPR;
+  if (row >= (int64_t)p.batch_heads * p.n) return;   // whole row groups exit together
+  const int bh = (int)(row / p.n);
+  const int tok = (int)(row - (int64_t)bh * p.n);
+  const int c = lane % CPR;
+  const int64_t off = slice_base(p, bh) + (int64_t)tok * p.stride_tok + c * 8;
+  const u32x4 o = *reinterpret_cast<const u32x4*>(p.out + off);
+  const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + off);
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += bf16_lo(o[e]) * bf16_lo(g[e]) + bf16_hi(o[e]) * bf16_hi(g[e]);
+#pragma unroll
+  for (int w = 1; w < CPR; w *= 2) s += __shfl_xor(s, w);
+  if (c == 0) p.dvec[row] = s;
+}
+
+// ---------------------------------------------------------------- dq
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
+  using T = BT<D>;
+  constexpr int kBuf = 2 * T::kRow + T::kTr;   // K rows, V rows, K^T
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int nQT = (p.m + kUnit - 1) / kUnit;
+  const int unit = xcd_unit(p.batch_heads * p.nW * nQT);
+  if (unit < 0) return;
+  const int qt = unit % nQT;
+  const int rest = unit / nQT;
+  const int win = rest % p.nW;
+  const int bh = rest / p.nW;
+  const int64_t base = slice_base(p, bh);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const uint32_t stb = (uint32_t)p.stride_tok * 2u;
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBuf);
+  for (int r = tid; r < p.m; r += kThreads) tab[r] = window_token(p.geo, win, r);
+  __syncthreads();
+
+  // this lane's query: Q and dO rows as B operands, its lse and Dv
+  const int qr = qt * kUnit + wave * 32 + l32;
+  const bool qvalid = qr < p.m;
+  const int qtok = qvalid ? tab[qr] : 0;
+  const uint32_t qoff = (uint32_t)qtok * stb;
+  u32x4 qreg[T::QS], dreg[T::QS];
+  {
+    const Rsrc rq = make_rsrc(p.q + base), rd = make_rsrc(p.dout + base);
+#pragma unroll
+    for (int s = 0; s < T::QS; ++s) {
+      const u32x4 a = buf_load16(rq, qoff + hf * D + s * 16, 0);
+      const u32x4 b = buf_load16(rd, qoff + hf * D + s * 16, 0);
+      qreg[s] = qvalid ? a : u32x4{0u, 0u, 0u, 0u};
+      dreg[s] = qvalid ? b : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const float lse2 = qvalid ? p.lse[(int64_t)bh * p.n + qtok] * kLog2e : INFINITY;
+  const float dval = qvalid ? p.dvec[(int64_t)bh * p.n + qtok] : 0.0f;
+  f32x16 acc[T::DB];
+#pragma unroll
+  for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
+
+  const int L = p.m + p.G;
+  const int nkt = (L + kBlk - 1) / kBlk;
+  const int lr = tid / T::CPR, lc = tid % T::CPR;
+  const bool loader = lr < kBlk;
+  const uint16_t* kmem = p.kmem + (int64_t)bh * p.G * D;
+  const uint16_t* vmem = p.vmem + (int64_t)bh * p.G * D;
+  u32x4 kx{}, vx{};
+  auto load_tile = [&](int tile) __attribute__((always_inline)) {
+    const int key = min(tile * kBlk + lr, L - 1);
+    if (key < p.m) {
+      const uint32_t off = (uint32_t)tab[key] * stb + lc * 16;
+      kx = buf_load16(make_rsrc(p.k + base), off, 0);
+      vx = buf_load16(make_rsrc(p.v + base), off, 0);
+    } else {
+      const uint32_t off = (uint32_t)(key - p.m) * (D * 2) + lc * 16;
+      kx = buf_load16(make_rsrc(kmem), off, 0);
+      vx = buf_load16(make_rsrc(vmem), off, 0);
+    }
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* sk = reinterpret_cast<uint16_t*>(smem + buf * kBuf);
+    uint16_t* sv = sk + kBlk * T::KS;
+    uint16_t* st = sv + kBlk * T::KS;
+    *reinterpret_cast<u32x4*>(sk + lr * T::KS + lc * 8) = kx;
+    *reinterpret_cast<u32x4*>(sv + lr * T::KS + lc * 8) = vx;
+    store_tr<T::TS>(st, lr, lc * 8, kx);
+  };
+  if (loader) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  const float c1 = p.c1;
+  for (int t = 0; t < nkt; ++t) {
+    if (loader && t + 1 < nkt) load_tile(t + 1);
+    const uint16_t* sk = reinterpret_cast<const uint16_t*>(smem + (t & 1) * kBuf);
+    const uint16_t* sv = sk + kBlk * T::KS;
+    const uint16_t* st = sv + kBlk * T::KS;
+    f32x16 s{}, dp{};
+#pragma unroll
+    for (int ss = 0; ss < T::QS; ++ss) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sk + l32 * T::KS + hf * (D / 2) + ss * 8);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(sv + l32 * T::KS + hf * (D / 2) + ss * 8);
+      s = mfma(a, qreg[ss], s);
+      dp = mfma(b, dreg[ss], dp);
+    }
+    u32x4 dsb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * u + j;
+        const int key = t * kBlk + acc_row(r, hf);
+        float x = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
+        x = key < L ? x : -INFINITY;
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lse2));
+        e[j] = pr * (dp[r] - dval);
+      }
+      dsb[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                     pack_bf16x2(e[6], e[7])};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(st + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+        acc[db] = mfma(a, dsb[u], acc[db]);
+      }
+    if (loader && t + 1 < nkt) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+  store_rows<D>(acc, p.scale, nullptr, p.dq + base, qoff, qvalid, hf);
+}
+
+// ---------------------------------------------------------------- dk, dv
+// MEM: memory-key units (b*h, memory chunk of 256 keys, query chunk) writing
+// fp32 partials; otherwise window-key units (b*h, window, key chunk of 256)
+// writing the final gradients.  PASS 0: dV; PASS 1: dK.
+template <int D, bool MEM, int PASS>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
+  using T = BT<D>;
+  // buffer: Q rows, then pass 0: dO^T; pass 1: dO rows and Q^T; then lse, Dv
+  constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
+  constexpr int kBuf = kMain + 2 * 32 * 4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int bh, kbase, nq, qbase = 0, win = 0;
+  if constexpr (MEM) {
+    const int nmc = (p.G + kUnit - 1) / kUnit;
+    const int unit = xcd_unit(p.batch_heads * nmc * p.nqc);
+    if (unit < 0) return;
+    const int qc = unit % p.nqc;
+    const int rest = unit / p.nqc;
+    kbase = (rest % nmc) * kUnit;
+    bh = rest / nmc;
+    qbase = qc * p.qchunk;
+    nq = min(p.qchunk, p.n - qbase);
+  } else {
+    const int nkc = (p.m + kUnit - 1) / kUnit;
+    const int unit = xcd_unit(p.batch_heads * p.nW * nkc);
+    if (unit < 0) return;
+    kbase = (unit % nkc) * kUnit;
+    const int rest = unit / nkc;
+    win = rest % p.nW;
+    bh = rest / p.nW;
+    nq = p.m;
+  }
+  const int64_t base = slice_base(p, bh);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const uint32_t stb = (uint32_t)p.stride_tok * 2u;
+  const int nkeys = MEM ? p.G : p.m;
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBuf);
+  if constexpr (!MEM) {
+    for (int r = tid; r < p.m; r += kThreads) tab[r] = window_token(p.geo, win, r);
+    __syncthreads();
+  }
+
+  // this lane's key: K (and V) rows as B operands
+  const int key = kbase + wave * 32 + l32;
+  const bool kvalid = key < nkeys;
+  const int kcl = min(key, nkeys - 1);
+  u32x4 kreg[T::QS], vreg[PASS == 1 ? T::QS : 1];
+  {
+    const uint16_t* ks = MEM ? p.kmem + (int64_t)bh * p.G * D : p.k + base;
+    const uint16_t* vs = MEM ? p.vmem + (int64_t)bh * p.G * D : p.v + base;
+    const uint32_t koff = MEM ? (uint32_t)kcl * (D * 2) : (uint32_t)tab[kcl] * stb;
+    const Rsrc rk = make_rsrc(ks), rv = make_rsrc(vs);
+#pragma unroll
+    for (int s = 0; s < T::QS; ++s) {
+      kreg[s] = buf_load16(rk, koff + hf * D + s * 16, 0);
+      if constexpr (PASS == 1) vreg[s] = buf_load16(rv, koff + hf * D + s * 16, 0);
+    }
+  }
+  f32x16 acc[T::DB];
+#pragma unroll
+  for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
+
+  const int nqb = (nq + kBlk - 1) / kBlk;
+  const int lr = tid / T::CPR, lc = tid % T::CPR;
+  const bool loader = lr < kBlk;
+  u32x4 qx{}, dx{};
+  float lx = INFINITY, dvx = 0.0f;
+  auto token_of = [&](int q) __attribute__((always_inline)) {
+    return MEM ? qbase + q : tab[q];
+  };
+  auto load_block = [&](int blk) __attribute__((always_inline)) {
+    if (loader) {
+      const int q = min(blk * kBlk + lr, nq - 1);
+      const uint32_t off = (uint32_t)token_of(q) * stb + lc * 16;
+      qx = buf_load16(make_rsrc(p.q + base), off, 0);
+      dx = buf_load16(make_rsrc(p.dout + base), off, 0);
+    }
+    if (tid < kBlk) {
+      const int q = blk * kBlk + tid;
+      const bool ok = q < nq;
+      const int64_t idx = (int64_t)bh * p.n + token_of(ok ? q : nq - 1);
+      lx = ok ? p.lse[idx] * kLog2e : INFINITY;   // a missing query gets P = 0
+      dvx = ok ? p.dvec[idx] : 0.0f;
+    }
+  };
+  auto store_block = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* b = smem + buf * kBuf;
+    uint16_t* sq = reinterpret_cast<uint16_t*>(b);
+    if (loader) {
+      *reinterpret_cast<u32x4*>(sq + lr * T::KS + lc * 8) = qx;
+      if constexpr (PASS == 0) {
+        store_tr<T::TS>(sq + kBlk * T::KS, lr, lc * 8, dx);          // dO^T
+      } else {
+        uint16_t* sdo = sq + kBlk * T::KS;
+        *reinterpret_cast<u32x4*>(sdo + lr * T::KS + lc * 8) = dx;   // dO rows
+        store_tr<T::TS>(sdo + kBlk * T::KS, lr, lc * 8, qx);         // Q^T
+      }
+    }
+    if (tid < kBlk) {
+      float* sl = reinterpret_cast<float*>(b + kMain);
+      sl[perm32(tid)] = lx;
+      sl[32 + perm32(tid)] = dvx;
+    }
+  };
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  const float c1 = p.c1;
+  const float bias = MEM ? p.mem_bias_raw : 0.0f;
+  for (int blk = 0; blk < nqb; ++blk) {
+    if (blk + 1 < nqb) load_block(blk + 1);
+    const unsigned char* b = smem + (blk & 1) * kBuf;
+    const uint16_t* sq = reinterpret_cast<const uint16_t*>(b);
+    const float* sl = reinterpret_cast<const float*>(b + kMain);
+    f32x16 s{};
+#pragma unroll
+    for (int ss = 0; ss < T::QS; ++ss) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sq + l32 * T::KS + hf * (D / 2) + ss * 8);
+      s = mfma(a, kreg[ss], s);
+    }
+    float pr[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + hf * 16 + r4 * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i] + bias, c1, -l4[i]));
+    }
+    if constexpr (PASS == 0) {
+      const uint16_t* sdt = sq + kBlk * T::KS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb{pack_bf16x2(pr[8 * u], pr[8 * u + 1]), pack_bf16x2(pr[8 * u + 2], pr[8 * u + 3]),
+                       pack_bf16x2(pr[8 * u + 4], pr[8 * u + 5]),
+                       pack_bf16x2(pr[8 * u + 6], pr[8 * u + 7])};
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(sdt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+          acc[db] = mfma(a, pb, acc[db]);
+        }
+      }
+    } else {
+      const uint16_t* sdo = sq + kBlk * T::KS;
+      const uint16_t* sqt = sdo + kBlk * T::KS;
+      f32x16 dp{};
+#pragma unroll
+      for (int ss = 0; ss < T::QS; ++ss) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sdo + l32 * T::KS + hf * (D / 2) + ss * 8);
+        dp = mfma(a, vreg[ss], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + hf * 16 + r4 * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb{pack_bf16x2(ds[8 * u], ds[8 * u + 1]), pack_bf16x2(ds[8 * u + 2], ds[8 * u + 3]),
+                       pack_bf16x2(ds[8 * u + 4], ds[8 * u + 5]),
+                       pack_bf16x2(ds[8 * u + 6], ds[8 * u + 7])};
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(sqt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+          acc[db] = mfma(a, pb, acc[db]);
+        }
+      }
+    }
+    if (blk + 1 < nqb) store_block((blk + 1) & 1);
+    __syncthreads();
+  }
+
+  if constexpr (MEM) {
+    // fp32 partials [bh][qc][key][d]; lane = key, registers = 4 consecutive d
+    if (kvalid) {
+      const int qc = qbase / p.qchunk;
+      float* dst = (PASS == 0 ? p.pv : p.pk) + (((int64_t)bh * p.nqc + qc) * p.G + key) * D;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * g + 4 * hf) =
+              f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+    }
+  } else {
+    const int tok = tab[kcl];
+    const float* add = nullptr;
+    if (p.G > 0) {
+      const int x = tok % p.geo.Wg;
+      const int y = (tok / p.geo.Wg) % p.geo.Hg;
+      const int t = tok / (p.geo.Wg * p.geo.Hg);
+      const int cell = ((t / p.pt) * p.Gy + y / p.py) * p.Gx + x / p.px;
+      add = (PASS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
+    }
+    store_rows<D>(acc, PASS == 0 ? 1.0f : p.scale, add, (PASS == 0 ? p.dv : p.dk) + base,
+                  (uint32_t)tok * stb, kvalid, hf);
+  }
+}
+
+// ---------------------------------------------------------------- memsum
+template <int D>
+__global__ void __launch_bounds__(256) bwd_memsum_kernel(BwdParams p, float inv_cell) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over bh, g, d
+  const int64_t per = (int64_t)p.G * D;
+  if (i >= (int64_t)p.batch_heads * per) return;
+  const int64_t bh = i / per, rest = i - bh * per;
+  float sk = 0.0f, sv = 0.0f;
+  for (int c = 0; c < p.nqc; ++c) {
+    const int64_t j = (bh * p.nqc + c) * per + rest;
+    sk += p.pk[j];
+    sv += p.pv[j];
+  }
+  p.gk[i] = sk * p.scale * inv_cell;
+  p.gv[i] = sv * inv_cell;
+}
+
+template <typename K>
+int set_lds(K kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return BASA_OK;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
+             ? BASA_OK
+             : BASA_ERR_HIP;
+}
+
+template <int D, bool MEM, int PASS>
+int launch_dkdv(const BwdParams& p, hipStream_t stream) {
+  using T = BT<D>;
+  constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
+  const size_t lds = 2 * (kMain + 2 * 32 * 4) + (MEM ? 0 : (size_t)p.m * 4);
+  if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
+  const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + kUnit - 1) / kUnit) * p.nqc
+                            : (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
+  if (units > INT32_MAX / 2) return BASA_ERR_UNSUPPORTED;
+  if (set_lds(&bwd_dkdv_kernel<D, MEM, PASS>, lds)) return BASA_ERR_HIP;
+  const int64_t upx = (units + 7) / 8;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MEM, PASS>), dim3((unsigned)(8 * upx)), dim3(kThreads),
+                     lds, stream, p);
+  return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
+template <int D>
+int launch_d(const BwdParams& p, hipStream_t stream) {
+  using T = BT<D>;
+  {
+    constexpr int CPR = D / 8, RPW = 64 / CPR;
+    const int64_t rows = (int64_t)p.batch_heads * p.n;
+    const int64_t blocks = (rows + 4 * RPW - 1) / (4 * RPW);
+    hipLaunchKernelGGL((bwd_dvec_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
+  }
+  int rc;
+  if (p.G > 0) {
+    if ((rc = launch_dkdv<D, true, 0>(p, stream))) return rc;
+    if ((rc = launch_dkdv<D, true, 1>(p, stream))) return rc;
+    const int64_t total = (int64_t)p.batch_heads * p.G * D;
+    hipLaunchKernelGGL((bwd_memsum_kernel<D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, p, 1.0f / (float)(p.pt * p.py * p.px));
+    if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
+  }
+  if ((rc = launch_dkdv<D, false, 0>(p, stream))) return rc;
+  if ((rc = launch_dkdv<D, false, 1>(p, stream))) return rc;
+  {
+    constexpr int kBuf = 2 * T::kRow + T::kTr;
+    const size_t lds = 2 * kBuf + (size_t)p.m * 4;
+    if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
+    const int64_t units = (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
+    if (set_lds(&bwd_dq_kernel<D>, lds)) return BASA_ERR_HIP;
+    const int64_t upx = (units + 7) / 8;
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(8 * upx)), dim3(kThreads), lds, stream,
+                       p);
+    if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
+  }
+  return BASA_OK;
+}
+
+}  // namespace
+
+int launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.head_dim == 128) return launch_d<128>(p, stream);
+  if (p.head_dim == 64) return launch_d<64>(p, stream);
+  return BASA_ERR_UNSUPPORTED;
+}
+
+}  // namespace basa

@@ -202,12 +202,14 @@ int basa_pool_kv(const void* k, const void* v, void* k_mem, void* v_mem, int32_t
   }
 }
 
-int basa_window_attn(const void* q, const void* k, const void* v, const void* k_mem,
-                     const void* v_mem, int64_t n_mem, void* out, int32_t batch, int32_t heads,
-                     int32_t head_dim, int32_t ndim, const int32_t* grid, const int32_t* window,
-                     const int32_t* shift, float scale, float mem_bias, int32_t dtype,
-                     int32_t layout, void* stream) {
-  try {
+namespace {
+
+int window_attn_impl(const void* q, const void* k, const void* v, const void* k_mem,
+                     const void* v_mem, int64_t n_mem, void* out, float* lse, int32_t batch,
+                     int32_t heads, int32_t head_dim, int32_t ndim, const int32_t* grid,
+                     const int32_t* window, const int32_t* shift, float scale, float mem_bias,
+                     int32_t dtype, int32_t layout, void* stream) {
+  {
     if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
@@ -238,8 +240,18 @@ int basa_window_attn(const void* q, const void* k, const void* v, const void* k_
     if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
         overlaps(out, tb, k_mem, mb) || overlaps(out, tb, v_mem, mb))
       return fail(BASA_ERR_INVALID_ARG, "out overlaps an input");
+    if (lse) {
+      if (dtype != BASA_BF16) return fail(BASA_ERR_UNSUPPORTED, "lse output needs dtype BASA_BF16");
+      if ((uintptr_t)lse % 4) return fail(BASA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+      const size_t lb = (size_t)batch * heads * n * 4;
+      if (overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) || overlaps(lse, lb, v, tb) ||
+          overlaps(lse, lb, out, tb) || overlaps(lse, lb, k_mem, mb) || overlaps(lse, lb, v_mem, mb))
+        return fail(BASA_ERR_INVALID_ARG, "lse overlaps an input or out");
+    }
 
     basa::AttnParams p{};
+    p.lse = lse;
+    p.n_tok = (int32_t)n;
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
     p.kmem = (const uint16_t*)k_mem; p.vmem = (const uint16_t*)v_mem; p.out = (uint16_t*)out;
     p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
@@ -265,8 +277,183 @@ int basa_window_attn(const void* q, const void* k, const void* v, const void* k_
     if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
     if (rc) return fail(rc, "window attention launch failed: %s", hipGetErrorString(hipGetLastError()));
     return ok();
+  }
+}
+
+}  // namespace
+
+int basa_window_attn(const void* q, const void* k, const void* v, const void* k_mem,
+                     const void* v_mem, int64_t n_mem, void* out, int32_t batch, int32_t heads,
+                     int32_t head_dim, int32_t ndim, const int32_t* grid, const int32_t* window,
+                     const int32_t* shift, float scale, float mem_bias, int32_t dtype,
+                     int32_t layout, void* stream) {
+  try {
+    return window_attn_impl(q, k, v, k_mem, v_mem, n_mem, out, nullptr, batch, heads, head_dim,
+                            ndim, grid, window, shift, scale, mem_bias, dtype, layout, stream);
   } catch (...) {
     return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn");
+  }
+}
+
+int basa_window_attn_fwd(const void* q, const void* k, const void* v, const void* k_mem,
+                         const void* v_mem, int64_t n_mem, void* out, float* lse, int32_t batch,
+                         int32_t heads, int32_t head_dim, int32_t ndim, const int32_t* grid,
+                         const int32_t* window, const int32_t* shift, float scale, float mem_bias,
+                         int32_t dtype, int32_t layout, void* stream) {
+  try {
+    if (!lse) return fail(BASA_ERR_INVALID_ARG, "lse must be non-NULL");
+    return window_attn_impl(q, k, v, k_mem, v_mem, n_mem, out, lse, batch, heads, head_dim, ndim,
+                            grid, window, shift, scale, mem_bias, dtype, layout, stream);
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn_fwd");
+  }
+}
+
+namespace {
+
+// Queries per memory-key unit of the backward (a multiple of 32).
+constexpr int64_t kBwdQueryChunk = 1024;
+
+struct BwdWorkspace {
+  size_t dvec, pk, pv, gk, gv, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdWorkspace bwd_workspace(int64_t bh, int64_t n, int64_t G, int32_t head_dim) {
+  BwdWorkspace w{};
+  const int64_t nqc = (n + kBwdQueryChunk - 1) / kBwdQueryChunk;
+  size_t off = 0;
+  w.dvec = off; off += align256((size_t)bh * n * 4);
+  const size_t part = G ? (size_t)bh * nqc * G * head_dim * 4 : 0;
+  const size_t red = G ? (size_t)bh * G * head_dim * 4 : 0;
+  w.pk = off; off += align256(part);
+  w.pv = off; off += align256(part);
+  w.gk = off; off += align256(red);
+  w.gv = off; off += align256(red);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+int64_t basa_window_attn_bwd_workspace(int32_t batch, int32_t heads, int32_t head_dim,
+                                       int32_t ndim, const int32_t* grid, const int32_t* pool) {
+  try {
+    if (batch < 1 || heads < 1 || (head_dim != 64 && head_dim != 128)) return -1;
+    int32_t g[3];
+    int64_t n;
+    if (check_grid(ndim, grid, g, &n)) return -1;
+    int64_t G = 0;
+    if (pool) {
+      int32_t pl[3];
+      if (check_divides(ndim, pool, g, pl, "pool")) return -1;
+      G = (int64_t)(g[0] / pl[0]) * (g[1] / pl[1]) * (g[2] / pl[2]);
+    }
+    ok();
+    return (int64_t)bwd_workspace((int64_t)batch * heads, n, G, head_dim).total;
+  } catch (...) {
+    return -1;
+  }
+}
+
+int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void* k_mem,
+                         const void* v_mem, const void* out, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, void* workspace, int64_t workspace_bytes,
+                         int32_t batch, int32_t heads, int32_t head_dim, int32_t ndim,
+                         const int32_t* grid, const int32_t* window, const int32_t* shift,
+                         const int32_t* pool, float scale, float mem_bias, int32_t dtype,
+                         int32_t layout, void* stream) {
+  try {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+      return fail(BASA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    if (dtype != BASA_BF16) return fail(BASA_ERR_UNSUPPORTED, "the backward needs dtype BASA_BF16");
+    int32_t g[3], w[3], s[3], pl[3] = {1, 1, 1};
+    int64_t n;
+    if ((rc = check_grid(ndim, grid, g, &n))) return rc;
+    if ((rc = check_divides(ndim, window, g, w, "window"))) return rc;
+    if ((rc = read3(ndim, shift, 0, s, "shift"))) return rc;
+    if ((pool == nullptr) != (k_mem == nullptr) || (k_mem == nullptr) != (v_mem == nullptr))
+      return fail(BASA_ERR_INVALID_ARG, "pool, k_mem and v_mem must all be given or all be NULL");
+    int64_t G = 0;
+    if (pool) {
+      if ((rc = check_divides(ndim, pool, g, pl, "pool"))) return rc;
+      G = (int64_t)(g[0] / pl[0]) * (g[1] / pl[1]) * (g[2] / pl[2]);
+    }
+    if (not_finite(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (not_finite(mem_bias)) return fail(BASA_ERR_INVALID_ARG, "mem_bias must be finite");
+    const int64_t m = (int64_t)w[0] * w[1] * w[2];
+    if (m > BASA_MAX_WINDOW_TOKENS)
+      return fail(BASA_ERR_UNSUPPORTED, "window of %lld tokens exceeds %d", (long long)m, BASA_MAX_WINDOW_TOKENS);
+    const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv, workspace};
+    for (const void* ptr : ptrs)
+      if (!aligned16(ptr)) return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (k_mem && (!aligned16(k_mem) || !aligned16(v_mem)))
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if ((uintptr_t)lse % 4) return fail(BASA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n, head_dim, &sb, &sh, &stok);
+    if (n * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit token offsets");
+    const BwdWorkspace ws = bwd_workspace((int64_t)batch * heads, n, G, head_dim);
+    if (workspace_bytes < (int64_t)ws.total)
+      return fail(BASA_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
+                  (long long)workspace_bytes, (long long)ws.total);
+    const size_t tb = (size_t)batch * heads * n * head_dim * 2;
+    const size_t mb = (size_t)batch * heads * G * head_dim * 2;
+    const size_t lb = (size_t)batch * heads * n * 4;
+    const void* ins[] = {q, k, v, out, dout};
+    const void* outs[] = {dq, dk, dv};
+    for (const void* o : outs) {
+      for (const void* i : ins)
+        if (overlaps(o, tb, i, tb)) return fail(BASA_ERR_INVALID_ARG, "an output overlaps an input");
+      if (overlaps(o, tb, k_mem, mb) || overlaps(o, tb, v_mem, mb) || overlaps(o, tb, lse, lb) ||
+          overlaps(o, tb, workspace, ws.total))
+        return fail(BASA_ERR_INVALID_ARG, "an output overlaps an input or the workspace");
+    }
+    if (overlaps(dq, tb, dk, tb) || overlaps(dq, tb, dv, tb) || overlaps(dk, tb, dv, tb))
+      return fail(BASA_ERR_INVALID_ARG, "dq, dk and dv overlap");
+    for (const void* i : ins)
+      if (overlaps(workspace, ws.total, i, tb))
+        return fail(BASA_ERR_INVALID_ARG, "the workspace overlaps an input");
+    if (overlaps(workspace, ws.total, lse, lb) || overlaps(workspace, ws.total, k_mem, mb) ||
+        overlaps(workspace, ws.total, v_mem, mb))
+      return fail(BASA_ERR_INVALID_ARG, "the workspace overlaps an input");
+
+    basa::BwdParams p{};
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.kmem = (const uint16_t*)k_mem; p.vmem = (const uint16_t*)v_mem;
+    p.out = (const uint16_t*)out; p.dout = (const uint16_t*)dout; p.lse = lse;
+    p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv;
+    char* wsb = (char*)workspace;
+    p.dvec = (float*)(wsb + ws.dvec);
+    p.pk = (float*)(wsb + ws.pk); p.pv = (float*)(wsb + ws.pv);
+    p.gk = (float*)(wsb + ws.gk); p.gv = (float*)(wsb + ws.gv);
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.n = (int32_t)n; p.m = (int32_t)m; p.G = (int32_t)G; p.nW = (int32_t)(n / m);
+    p.qchunk = (int32_t)kBwdQueryChunk;
+    p.nqc = (int32_t)((n + kBwdQueryChunk - 1) / kBwdQueryChunk);
+    p.scale = resolve_scale(scale, head_dim);
+    p.c1 = p.scale * basa::kLog2e;
+    p.mem_bias_raw = G ? mem_bias / p.scale : 0.0f;
+    basa::Geometry& geo = p.geo;
+    geo.T = g[0]; geo.Hg = g[1]; geo.Wg = g[2];
+    geo.wt = w[0]; geo.wy = w[1]; geo.wx = w[2];
+    geo.st = ((s[0] % w[0]) + w[0]) % w[0];
+    geo.sy = ((s[1] % w[1]) + w[1]) % w[1];
+    geo.sx = ((s[2] % w[2]) + w[2]) % w[2];
+    geo.nwy = g[1] / w[1];
+    geo.nwx = g[2] / w[2];
+    p.pt = pl[0]; p.py = pl[1]; p.px = pl[2];
+    p.Gy = g[1] / pl[1]; p.Gx = g[2] / pl[2];
+    rc = basa::launch_attn_bwd(p, (hipStream_t)stream);
+    if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "backward launch shape not supported");
+    if (rc) return fail(rc, "backward launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn_bwd");
   }
 }
 

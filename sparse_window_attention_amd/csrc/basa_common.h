@@ -56,6 +56,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Slot of row `key` in a transposed tile whose rows are the k index of an
+// MFMA fed from an S accumulator (V^T in the forward; K^T, Q^T, dO^T in the
+// backward): within each group of 16, the order matches how the
+// accumulator registers map onto the k index of the product's operand.
+__device__ __forceinline__ int vslot(int key) {
+  const int a = key >> 2, i = key & 3;
+  return (a >> 2) * 16 + (a & 1) * 8 + ((a >> 1) & 1) * 4 + i;
+}
+
+// Raw buffer resource over a (batch, head) slice: wave-uniform base in
+// scalar registers, per-lane 32-bit byte offsets (every offset inside a slice
+// is below 2^32 bytes, checked on the host).
+using Rsrc = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFFu,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

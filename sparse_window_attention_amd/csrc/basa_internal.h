@@ -35,6 +35,8 @@ struct AttnParams {
   float mem_bias_raw;     // memory logit bias divided by the scale
   float mem_bias;         // memory logit bias (natural log units)
   Geometry geo;
+  float* lse;             // optional [B*H, n_tok] fp32 natural-log log-sum-exp of every query
+  int32_t n_tok;          // tokens per (batch, head): the lse row length
 };
 
 struct PoolParams {
@@ -49,6 +51,37 @@ struct PoolParams {
   int32_t pt, py, px;
   int32_t Gt, Gy, Gx, G;
 };
+
+// Arguments of the backward of window attention (bf16).  Element strides as
+// in AttnParams; lse, dvec and the workspaces are fp32.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* kmem;   // pooled memory of k, v ([B, H, G, D]); unused when G = 0
+  const uint16_t* vmem;
+  const uint16_t* out;    // forward output
+  const uint16_t* dout;   // gradient of the output
+  const float* lse;       // [B*H, n] natural-log log-sum-exp from the forward
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;            // workspace [B*H, n]: row sums of dout * out
+  float* pk;              // workspace [B*H, nqc, G, D]: memory-key partial gradients
+  float* pv;
+  float* gk;              // workspace [B*H, G, D]: memory gradients over the cell size
+  float* gv;              //   (gk also carries the softmax scale)
+  int64_t stride_b, stride_h;
+  int32_t stride_tok;
+  int32_t heads, batch_heads, head_dim;
+  int32_t n, m, G, nW;
+  int32_t qchunk, nqc;    // memory-key units: queries per chunk, chunks per head
+  float c1, scale, mem_bias_raw;
+  Geometry geo;
+  int32_t pt, py, px, Gy, Gx;  // pool cells (G = 0: no memory)
+};
+
+int launch_attn_bwd(const BwdParams& p, hipStream_t stream);
 
 int launch_attn_bf16(const AttnParams& p, bool full, hipStream_t stream);
 int launch_attn_f32(const AttnParams& p, bool full, hipStream_t stream);

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(S.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -163,3 +163,62 @@ def test_single_hip_runtime_in_process():
                        timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "1"
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + SZ, v=FAKE + 2 * SZ, km=FAKE + 3 * SZ, vm=FAKE + 4 * SZ,
+             out=FAKE + 5 * SZ, dout=FAKE + 6 * SZ, lse=FAKE + 7 * SZ, dq=FAKE + 8 * SZ,
+             dk=FAKE + 9 * SZ, dv=FAKE + 10 * SZ, ws=FAKE + 11 * SZ, wsb=1 << 28, B=1, H=2,
+             D=128, grid=(8, 8), window=(4, 4), shift=(0, 0), pool=(4, 4), scale=-1.0,
+             bias=0.0, dtype=S.BASA_BF16, layout=S.BASA_LAYOUT_BHND)
+    a.update(kw)
+    arr = lambda x: None if x is None else (ctypes.c_int32 * len(x))(*x)
+    return S.lib.basa_window_attn_bwd(
+        a["q"], a["k"], a["v"], a["km"], a["vm"], a["out"], a["dout"], a["lse"], a["dq"],
+        a["dk"], a["dv"], a["ws"], a["wsb"], a["B"], a["H"], a["D"], len(a["grid"]),
+        arr(a["grid"]), arr(a["window"]), arr(a["shift"]), arr(a["pool"]), a["scale"],
+        a["bias"], a["dtype"], a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), S.BASA_ERR_INVALID_ARG),
+    (dict(lse=None), S.BASA_ERR_INVALID_ARG),
+    (dict(ws=None), S.BASA_ERR_INVALID_ARG),
+    (dict(pool=None), S.BASA_ERR_INVALID_ARG),                    # memory without pool
+    (dict(km=None, vm=None), S.BASA_ERR_INVALID_ARG),             # pool without memory
+    (dict(pool=(3, 4)), S.BASA_ERR_INVALID_ARG),                  # pool does not divide
+    (dict(window=(3, 4)), S.BASA_ERR_INVALID_ARG),
+    (dict(wsb=1024), S.BASA_ERR_INVALID_ARG),                     # workspace too small
+    (dict(dq=FAKE + 64), S.BASA_ERR_INVALID_ARG),                 # dq overlaps q
+    (dict(dk=FAKE + 8 * SZ + 128), S.BASA_ERR_INVALID_ARG),       # dk overlaps dq
+    (dict(ws=FAKE + 7 * SZ), S.BASA_ERR_INVALID_ARG),             # workspace overlaps lse
+    (dict(lse=FAKE + 7 * SZ + 2), S.BASA_ERR_INVALID_ARG),        # misaligned lse
+    (dict(dtype=S.BASA_F32), S.BASA_ERR_UNSUPPORTED),
+    (dict(D=96), S.BASA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), S.BASA_ERR_INVALID_ARG),
+])
+def test_backward_validation(kw, code):
+    assert _bwd(**kw) == code
+    assert len(S.lib.basa_last_error().decode()) > 5
+
+
+def test_backward_workspace_size():
+    f = S.lib.basa_window_attn_bwd_workspace
+    arr = lambda x: (ctypes.c_int32 * len(x))(*x)
+    no_mem = f(1, 24, 128, 2, arr((128, 128)), None)
+    with_mem = f(1, 24, 128, 2, arr((128, 128)), arr((8, 8)))
+    assert no_mem >= 24 * 16384 * 4                     # one fp32 per token
+    # memory partials: two fp32 [B*H, chunks of 1024 queries, G, D] and their sums
+    assert with_mem >= no_mem + 2 * 24 * 16 * 256 * 128 * 4 + 2 * 24 * 256 * 128 * 4
+    assert f(1, 24, 128, 2, arr((128, 128)), arr((3, 8))) == -1
+    assert f(1, 24, 96, 2, arr((128, 128)), None) == -1
+
+
+def test_fwd_lse_validation():
+    f = S.lib.basa_window_attn_fwd
+    arr = lambda x: (ctypes.c_int32 * len(x))(*x)
+    args = [FAKE, FAKE + SZ, FAKE + 2 * SZ, None, None, 0, FAKE + 3 * SZ]
+    rest = [1, 2, 128, 2, arr((8, 8)), arr((4, 4)), arr((0, 0)), -1.0, 0.0]
+    assert f(*args, None, *rest, S.BASA_BF16, 0, None) == S.BASA_ERR_INVALID_ARG
+    assert f(*args, FAKE + 4 * SZ, *rest, S.BASA_F32, 0, None) == S.BASA_ERR_UNSUPPORTED
+    assert f(*args, FAKE + 3 * SZ + 64, *rest, S.BASA_BF16, 0, None) == S.BASA_ERR_INVALID_ARG

@@ -1,0 +1,100 @@
+"""GPU parity of the backward (forward with log-sum-exp, then gradients)
+through the C ABI against the backward oracle.
+
+Bars: lse within 2e-3 (absolute, natural log) of the fp64 oracle.  For each
+gradient, with R the largest |oracle value|: max |error| <= 3e-2 R and mean
+|error| <= 3e-3 R.  The kernels round P and dS to bf16 (relative 2^-9) as
+MFMA operands and write bf16 gradients (relative 2^-9); everything else
+accumulates in fp32 -- a few bf16 half-ulps of the largest entry bound the
+error.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import bhnd_to_bnhd, log, random_qkv, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+S = pytest.importorskip("sparse_window_attention_amd")
+
+MAX_REL, MEAN_REL = 3e-2, 3e-3
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    R = float(np.abs(ref).max())
+    err = np.abs(got - ref)
+    log(f"{what}: max |ref| {R:.3e}  max err {err.max():.3e} ({err.max() / R:.2e} R)  "
+        f"mean err {err.mean():.3e} ({err.mean() / R:.2e} R)")
+    assert err.max() <= MAX_REL * R and err.mean() <= MEAN_REL * R, (what, err.max() / R,
+                                                                       err.mean() / R)
+
+
+CASES = [
+    # name, B, H, D, grid, window, shift, pool, bias, layout
+    ("2d pool", 2, 3, 128, (24, 40), (12, 20), (5, 13), (4, 8), 0.0, "bhnd"),
+    ("2d no memory", 2, 3, 128, (16, 48), (16, 16), (8, 3), None, 0.0, "bhnd"),
+    ("3d pool", 1, 3, 128, (6, 10, 26), (3, 5, 13), (1, 3, 7), (3, 5, 2), 0.0, "bhnd"),
+    ("head dim 64, bias", 1, 4, 64, (16, 32), (8, 8), (3, 5), (4, 4), math.log(16.0), "bhnd"),
+    ("bnhd", 2, 2, 128, (16, 32), (8, 16), (4, 9), (4, 8), 0.0, "bnhd"),
+    ("query chunks", 1, 2, 128, (32, 48), (16, 16), (8, 8), (8, 8), 0.0, "bhnd"),
+    ("window 400", 1, 2, 128, (40, 40), (20, 20), (10, 7), (8, 8), 0.0, "bhnd"),
+    ("memory 1024", 1, 2, 128, (64, 64), (16, 16), (8, 8), (2, 2), 0.0, "bhnd"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_backward_parity(case):
+    name, B, H, D, grid, window, shift, pool, bias, layout = CASES[case]
+    n = int(np.prod(grid))
+    log(f"backward '{name}': B={B} H={H} D={D} grid={grid} window={window} pool={pool}")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=500 + case)
+    (do,) = random_qkv((B, H, n, D), "bf16", seed=600 + case)[:1]
+    ref = O.window_attention_backward(q, k, v, do, grid, window, shift, pool,
+                                      mem_logit_bias=bias)
+    conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)
+    qg, kg, vg, dog = (to_gpu(conv(x), "bf16") for x in (q, k, v, do))
+    mem = S.pool_kv(kg, vg, grid, pool, layout=layout) if pool is not None else None
+    out, lse = S.window_attn_fwd(qg, kg, vg, grid, window, shift, mem=mem, mem_bias=bias,
+                                 layout=layout)
+    dq, dk, dv = S.window_attn_bwd(qg, kg, vg, out, dog, lse, grid, window, shift, mem=mem,
+                                   pool=pool, mem_bias=bias, layout=layout)
+    torch.cuda.synchronize()
+    back = (lambda x: x.transpose(0, 2, 1, 3)) if layout == "bnhd" else (lambda x: x)
+    lerr = np.abs(lse.double().cpu().numpy() - ref["lse"]).max()
+    log(f"{name}: lse max err {lerr:.2e}")
+    assert lerr <= 2e-3
+    for g, key in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        check_grad(back(to_np(g)), ref[key], f"{name} {key}")
+
+
+def test_forward_with_lse_matches_plain_forward():
+    grid, window, shift, pool = (16, 32), (8, 8), (3, 5), (4, 4)
+    n = 512
+    q, k, v = random_qkv((1, 2, n, 128), "bf16", seed=77)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool)
+    a = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem)
+    b, _ = S.window_attn_fwd(qg, kg, vg, grid, window, shift, mem=mem)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_backward_deterministic():
+    grid, window, shift, pool = (32, 48), (16, 16), (8, 8), (8, 8)
+    n = 1536
+    q, k, v, do = random_qkv((1, 2, n, 128), "bf16", seed=88) + random_qkv((1, 2, n, 128), "bf16", seed=89)[:1]
+    qg, kg, vg, dog = (to_gpu(x, "bf16") for x in (q, k, v, do))
+    mem = S.pool_kv(kg, vg, grid, pool)
+    out, lse = S.window_attn_fwd(qg, kg, vg, grid, window, shift, mem=mem)
+    g1 = S.window_attn_bwd(qg, kg, vg, out, dog, lse, grid, window, shift, mem=mem, pool=pool)
+    g2 = S.window_attn_bwd(qg, kg, vg, out, dog, lse, grid, window, shift, mem=mem, pool=pool)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
