@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=("window", "dense", "copy", "all"), default="all",
+    ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "all"), default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
                          "at the same shape; 'copy': a plain device copy of known size, the "
                          "calibration for hardware byte counters (all three for profilers)")
@@ -359,6 +359,49 @@ def measure_composition(S, wl, sets, steps, stream):
     return r
 
 
+def measure_backward(S, wl, sets, steps, stream):
+    """Times the training-side pair at the headline shape: the forward that
+    also writes the log-sum-exp, then the backward (gradients of Q, K, V with
+    the pooled memory's gradient folded back).  Algorithmic backward work:
+    five products per window (S, dP, dV, dK, dQ), 10*B*H*n*(m+G)*D flops."""
+    import torch
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    m, G = wl.window_tokens, wl.mem_tokens
+    dev = sets[0][0].device
+    douts = [torch.randn_like(s[0]) for s in sets]
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(s[0]) for s in sets]
+    grads = tuple(torch.empty_like(sets[0][0]) for _ in range(3))
+    ws = torch.empty(S.bwd_workspace_bytes(B, H, D, wl.grid, wl.pool), dtype=torch.uint8,
+                     device=dev)
+    fwd, bwd = [], []
+    for i in range(steps + 3):
+        q, k, v = sets[i % len(sets)]
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        mem = S.pool_kv(k, v, wl.grid, wl.pool)
+        ev[0].record(stream)
+        out, _ = S.window_attn_fwd(q, k, v, wl.grid, wl.window, shift, mem=mem,
+                                   out=outs[i % len(sets)], lse=lse)
+        ev[1].record(stream)
+        S.window_attn_bwd(q, k, v, out, douts[i % len(sets)], lse, wl.grid, wl.window, shift,
+                          mem=mem, pool=wl.pool, grads=grads, workspace=ws)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            fwd.append(ev[0].elapsed_time(ev[1]))
+            bwd.append(ev[1].elapsed_time(ev[2]))
+    fl = 10 * B * H * n * (m + G) * D
+    f_ms, b_ms = sum(fwd) / len(fwd), sum(bwd) / len(bwd)
+    return {"workload": wl.name, "forward_with_lse_ms": f_ms, "backward_ms": b_ms,
+            "backward_algorithmic_flops": fl,
+            "backward_tflops": fl / (b_ms * 1e-3) / 1e12,
+            "backward_mfma_frac": fl / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "workspace_bytes": ws.numel(),
+            "note": "backward = dvec, memory-key dV/dK partials, their sum, window-key dV/dK "
+                    "(pooled memory gradient folded in), dQ"}
+
+
 def measure_window(S, wl, args, stream, dev, with_dense=True):
     n, m, G, D, H, B = (wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.heads,
                        wl.batch)
@@ -441,6 +484,10 @@ def main():
         print(json.dumps({"copy_bytes": COPY_BYTES, "copy_ms": median(ts),
                           "copy_gbs": 2 * COPY_BYTES / (median(ts) * 1e-3) / 1e9}))
         return
+    if args.only == "backward":
+        sets = make_sets(head, 2, dev)
+        print(json.dumps(measure_backward(S, head, sets, args.steps, stream)))
+        return
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
         ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)
@@ -459,6 +506,12 @@ def main():
     print(f"[bench] composition baseline: gather {comp['gather']*1e3:.1f} + attention "
           f"{comp['attention']*1e3:.1f} + scatter {comp['scatter']*1e3:.1f} + broadcast "
           f"{comp['broadcast']*1e3:.1f} us", file=sys.stderr, flush=True)
+    bwd_sets = make_sets(head, 2, dev)
+    bwd = measure_backward(S, head, bwd_sets, max(8, args.steps // 4), stream)
+    del bwd_sets
+    print(f"[bench] backward ({head.name}): forward+lse {bwd['forward_with_lse_ms']*1e3:.1f} us, "
+          f"backward {bwd['backward_ms']*1e3:.1f} us ({bwd['backward_tflops']:.0f} TFLOP/s)",
+          file=sys.stderr, flush=True)
     res_o = measure_window(S, other, args, stream, dev)
     print(f"[bench] {other.name}: attn {res_o['window_attn_ms']['mean']*1e3:.1f} us "
           f"({res_o['window_attn_tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
@@ -507,6 +560,7 @@ def main():
         "ms_per_attn_call": res["window_attn_ms"]["mean"],
         "windows": {f"{res['m']}": res, f"{res_o['m']}": res_o},
         "composition_baseline": comp,
+        "backward": bwd,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
