@@ -12,3 +12,6 @@ from .basa_oracle import (  # noqa: F401
 from .basa_backward import (  # noqa: F401
     attention_backward_rows, pool_backward, window_attention_backward,
     window_attention_backward_head)
+from .basa_curve import (  # noqa: F401
+    center_region, curve_attention, curve_attention_bruteforce, hilbert_curve_xy,
+    hilbert_order)
