@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "all"), default="all",
+    ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "hilbert", "all"),
+                    default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
                          "at the same shape; 'copy': a plain device copy of known size, the "
                          "calibration for hardware byte counters (all three for profilers)")
@@ -402,6 +403,66 @@ def measure_backward(S, wl, sets, steps, stream):
                     "(pooled memory gradient folded in), dQ"}
 
 
+HILBERT_SIDES = (64, 128)    # token grids of 1024 x 1024 and 2048 x 2048 px images
+HILBERT_TILE = 256
+HILBERT_REGION = (8, 8)
+
+
+def measure_hilbert(S, stream, dev, steps):
+    """Attention in tiles of 256 consecutive Hilbert-curve positions, sliding
+    half a tile from call to call, with an 8 x 8 central region as memory,
+    against the in-build dense kernel at the same shape (B=1, 24 heads,
+    D=128).  A step is the region gather plus the tile attention."""
+    import torch
+    res = {}
+    for side in HILBERT_SIDES:
+        n, B, H, D = side * side, 1, 24, 128
+        g = torch.Generator(device=dev)
+        g.manual_seed(4000 + side)
+        sets = [tuple(torch.randn((B, H, n, D), generator=g, device=dev).to(torch.bfloat16)
+                      for _ in range(3)) for _ in range(2)]
+        order = torch.from_numpy(S.hilbert_order(side)).to(dev)
+        reg = torch.from_numpy(S.center_region_tokens((side, side), HILBERT_REGION)).to(dev)
+        G = reg.numel()
+        out = torch.empty_like(sets[0][0])
+        mem = tuple(torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev) for _ in range(2))
+        gat, att, att0 = [], [], []
+        for i in range(steps + 3):
+            q, k, v = sets[i % 2]
+            slide = (i % 2) * HILBERT_TILE // 2
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(stream)
+            S.gather_kv(k, v, reg, out=mem)
+            ev[1].record(stream)
+            S.curve_attn(q, k, v, order, HILBERT_TILE, slide, mem=mem, out=out)
+            ev[2].record(stream)
+            S.curve_attn(q, k, v, order, HILBERT_TILE, slide, out=out)
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            if i >= 3:
+                gat.append(ev[0].elapsed_time(ev[1]))
+                att.append(ev[1].elapsed_time(ev[2]))
+                att0.append(ev[2].elapsed_time(ev[3]))
+        dense_ms = median(time_dense(S, sets, 3, stream))
+        g_ms, a_ms, a0_ms = (sum(x) / len(x) for x in (gat, att, att0))
+        fl = window_flops(B, H, n, HILBERT_TILE, G, D)
+        res[f"{side}x{side}"] = {
+            "n": n, "tile": HILBERT_TILE, "region_tokens": G,
+            "gather_ms": g_ms, "tile_attn_ms": a_ms, "tile_attn_nomem_ms": a0_ms,
+            "tile_attn_tflops": fl / (a_ms * 1e-3) / 1e12,
+            "dense_ms": dense_ms,
+            "speedup_vs_dense": dense_ms / (g_ms + a_ms),
+            "speedup_vs_dense_nomem": dense_ms / a0_ms,
+            "theoretical_n_over_tile_plus_region": n / (HILBERT_TILE + G),
+            "theoretical_n_over_tile": n / HILBERT_TILE,
+        }
+        del sets
+    res["note"] = ("tile = 256 consecutive Hilbert positions, slide 0 / 128 alternating, "
+                   "8x8 central region gathered as memory keys; the page's 2.3x (1024^2 px) "
+                   "and 4.17x (2048^2 px) are context (its tile and region sizes are not stated)")
+    return res
+
+
 def measure_window(S, wl, args, stream, dev, with_dense=True):
     n, m, G, D, H, B = (wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.heads,
                        wl.batch)
@@ -488,6 +549,9 @@ def main():
         sets = make_sets(head, 2, dev)
         print(json.dumps(measure_backward(S, head, sets, args.steps, stream)))
         return
+    if args.only == "hilbert":
+        print(json.dumps(measure_hilbert(S, stream, dev, args.steps)))
+        return
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
         ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)
@@ -512,6 +576,10 @@ def main():
     print(f"[bench] backward ({head.name}): forward+lse {bwd['forward_with_lse_ms']*1e3:.1f} us, "
           f"backward {bwd['backward_ms']*1e3:.1f} us ({bwd['backward_tflops']:.0f} TFLOP/s)",
           file=sys.stderr, flush=True)
+    hil = measure_hilbert(S, stream, dev, max(8, args.steps // 4))
+    print("[bench] hilbert tiles: " + ", ".join(
+        f"{k} {v['tile_attn_ms']*1e3:.1f} us ({v['speedup_vs_dense']:.2f}x vs dense)"
+        for k, v in hil.items() if k != "note"), file=sys.stderr, flush=True)
     res_o = measure_window(S, other, args, stream, dev)
     print(f"[bench] {other.name}: attn {res_o['window_attn_ms']['mean']*1e3:.1f} us "
           f"({res_o['window_attn_tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
@@ -561,6 +629,7 @@ def main():
         "windows": {f"{res['m']}": res, f"{res_o['m']}": res_o},
         "composition_baseline": comp,
         "backward": bwd,
+        "hilbert_tiles": hil,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

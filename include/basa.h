@@ -17,6 +17,10 @@
  *            the method's four parts and on its complexity.
  *   [SFA]    Scale-Free Attention abstract (artificialintelbulletin.com):
  *            mean pooling, token-count correction, one shared softmax.
+ *   [HilbertA] "HilbertA: Hilbert Attention for Image Generation with
+ *            Diffusion Models", catalogue record (info.umar.mx), abstract:
+ *            Hilbert-curve token order, tiles along it, a sliding schedule,
+ *            a small shared central region.
  *
  * Conventions shared by every call
  *   - Plain C types only; device buffers are raw device pointers, shape and
@@ -211,6 +215,54 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v,
                          const int32_t* shift, const int32_t* pool,
                          float scale, float mem_bias,
                          int32_t dtype, int32_t layout, void* stream);
+
+/*
+ * Token order along a Hilbert curve of a side x side grid [HilbertA,
+ * abstract: tokens reordered along Hilbert curves keep 2D neighbourhoods in a
+ * contiguous layout]: order_out[d] = y*side + x of curve position d, starting
+ * at (0, 0); consecutive positions are grid neighbours and every aligned run
+ * of 4^k positions covers a 2^k x 2^k square.  Writes side*side ints (host).
+ * Errors: INVALID_ARG for NULL or side not a power of two in [1, 32768].
+ */
+int basa_hilbert_order(int32_t side, int32_t* order_out);
+
+/*
+ * Row gather: k_out[b,h,i,:] = k[b,h,idx[i],:] and the same for v -- the
+ * keys of a shared region (HilbertA's small central region every tile also
+ * attends to) as the memory operand of basa_curve_attn.
+ *   k, v          device, B x H x n_tokens x D in `layout`
+ *   idx           device int32 [n_idx] token indices (clamped into range)
+ *   k_out, v_out  device [B, H, n_idx, D] contiguous
+ * Errors: INVALID_ARG (NULL, sizes, alignment, an output overlapping an
+ * input), UNSUPPORTED (dtype, head_dim).
+ */
+int basa_gather_kv(const void* k, const void* v, const int32_t* idx, int64_t n_idx,
+                   void* k_out, void* v_out, int32_t batch, int32_t heads,
+                   int32_t head_dim, int64_t n_tokens, int32_t dtype, int32_t layout,
+                   void* stream);
+
+/*
+ * Attention inside tiles of an explicit token order, with the same kernels
+ * and optional memory as basa_window_attn [HilbertA, abstract: contiguous
+ * tiles along the curve, a sliding schedule across layers, a shared central
+ * region].  Tile j holds the tokens order[(j*tile + slide + r) mod n],
+ * r < tile; every query attends to its tile's keys followed by the n_mem
+ * memory keys under one softmax.  With the raster order this is window
+ * attention over a grid of n/tile rows of `tile` tokens.
+ *   order    device int32 [n_tokens]: a permutation of 0..n-1 (entries out
+ *            of range are clamped; a non-permutation gives a well-defined
+ *            but meaningless result)
+ *   tile     divides n_tokens, <= BASA_MAX_WINDOW_TOKENS
+ *   slide    any integer, reduced modulo n_tokens
+ *   other arguments as basa_window_attn (n_tokens in place of the grid)
+ * Errors: INVALID_ARG, UNSUPPORTED as basa_window_attn.
+ */
+int basa_curve_attn(const void* q, const void* k, const void* v,
+                    const void* k_mem, const void* v_mem, int64_t n_mem, void* out,
+                    int32_t batch, int32_t heads, int32_t head_dim, int64_t n_tokens,
+                    const int32_t* order, int32_t tile, int64_t slide,
+                    float scale, float mem_bias, int32_t dtype, int32_t layout,
+                    void* stream);
 
 /*
  * Dense full attention out = softmax(scale * q k^T) v over all n_tokens keys

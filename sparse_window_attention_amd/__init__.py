@@ -19,6 +19,7 @@ __all__ = [
     "SCHED_NONE", "SCHED_ALTERNATE", "SCHED_FOUR_PHASE", "BasaError", "lib",
     "library_path", "version", "mem_tokens", "shift_for_block", "pool_kv",
     "window_attn", "window_attn_fwd", "window_attn_bwd", "bwd_workspace_bytes", "full_attn",
+    "hilbert_order", "center_region_tokens", "gather_kv", "curve_attn",
 ]
 
 BASA_OK, BASA_ERR_INVALID_ARG, BASA_ERR_UNSUPPORTED, BASA_ERR_HIP = 0, 1, 2, 3
@@ -68,6 +69,11 @@ def _load() -> ctypes.CDLL:
         "basa_window_attn_fwd": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32,
                                                 i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
         "basa_window_attn_bwd_workspace": (i64, [i32, i32, i32, i32, pi32, pi32]),
+        "basa_hilbert_order": (ctypes.c_int, [i32, pi32]),
+        "basa_gather_kv": (ctypes.c_int, [vp, vp, vp, i64, vp, vp, i32, i32, i32, i64, i32, i32,
+                                          vp]),
+        "basa_curve_attn": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i64, vp,
+                                           i32, i64, f32, f32, i32, i32, vp]),
         "basa_window_attn_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 i64, i32, i32, i32, i32, pi32, pi32, pi32, pi32,
                                                 f32, f32, i32, i32, vp]),
@@ -321,4 +327,73 @@ def full_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "b
         raise ValueError("scale must be positive")
     _check(lib.basa_full_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n,
                               D, s, _dtype_code(q), lay, _stream(q)))
+    return out
+
+
+# ------------------------------------------------------- Hilbert-order tiles
+def hilbert_order(side: int):
+    """Raster token index of every position of the Hilbert curve over a
+    side x side grid (host numpy int32 [side*side])."""
+    import numpy as np
+    out = np.empty(int(side) * int(side), dtype=np.int32)
+    _check(lib.basa_hilbert_order(int(side), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return out
+
+
+def center_region_tokens(grid: Sequence[int], size: Sequence[int]):
+    """Raster indices of the size[0] x size[1] block at the centre of a 2-D
+    grid (rows and columns starting at (grid - size) // 2), host numpy int32."""
+    import numpy as np
+    Hg, Wg = (int(x) for x in grid)
+    ch, cw = (int(x) for x in size)
+    y0, x0 = (Hg - ch) // 2, (Wg - cw) // 2
+    ys, xs = np.meshgrid(np.arange(y0, y0 + ch), np.arange(x0, x0 + cw), indexing="ij")
+    return (ys * Wg + xs).reshape(-1).astype(np.int32)
+
+
+def gather_kv(k, v, idx, layout: str = "bhnd", out: Optional[tuple] = None):
+    """(k[:, :, idx], v[:, :, idx]) as [B, H, len(idx), D] tensors; idx is an
+    int32 tensor on the GPU."""
+    torch = _torch()
+    _check_tensors(k, v)
+    B, H, n, D, lay = _layout_dims(k, layout)
+    if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.dim() != 1:
+        raise ValueError("idx must be a contiguous int32 vector on the GPU")
+    G = idx.numel()
+    if out is None:
+        ko = torch.empty((B, H, G, D), dtype=k.dtype, device=k.device)
+        vo = torch.empty_like(ko)
+    else:
+        ko, vo = out
+        _check_tensors(k, ko, vo)
+        if tuple(ko.shape) != (B, H, G, D) or tuple(vo.shape) != (B, H, G, D):
+            raise ValueError(f"gather outputs must have shape {(B, H, G, D)}")
+    _check(lib.basa_gather_kv(k.data_ptr(), v.data_ptr(), idx.data_ptr(), G, ko.data_ptr(),
+                              vo.data_ptr(), B, H, D, n, _dtype_code(k), lay, _stream(k)))
+    return ko, vo
+
+
+def curve_attn(q, k, v, order, tile: int, slide: int = 0, mem: Optional[tuple] = None,
+               scale: Optional[float] = None, mem_bias: float = 0.0, out=None,
+               layout: str = "bhnd"):
+    """Attention inside tiles of `tile` consecutive positions of a token order
+    (int32 tensor [n] on the GPU, e.g. hilbert_order), slid by `slide`
+    positions, with optional memory keys (e.g. gather_kv of a shared region)."""
+    torch = _torch()
+    _check_tensors(q, k, v)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v shapes differ")
+    if order.dtype != torch.int32 or not order.is_cuda or order.numel() != n \
+            or not order.is_contiguous():
+        raise ValueError("order must be a contiguous int32 [n] tensor on the GPU")
+    out = torch.empty_like(q) if out is None else out
+    _check_tensors(q, out)
+    km_p, vm_p, G = _mem_args(q, mem, B, H, D)
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_curve_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, G,
+                               out.data_ptr(), B, H, D, n, order.data_ptr(), int(tile),
+                               int(slide), s, float(mem_bias), _dtype_code(q), lay, _stream(q)))
     return out

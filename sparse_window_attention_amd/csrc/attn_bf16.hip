@@ -157,7 +157,7 @@ struct Core {
 
   // byte offsets of the window's tokens inside the (batch, head) slice
   __device__ __forceinline__ void build_table(uint32_t* t, int win) const {
-    for (int r = tid; r < m; r += TL::kThreads) t[r] = (uint32_t)window_token(p.geo, win, r) * stb;
+    for (int r = tid; r < m; r += TL::kThreads) t[r] = (uint32_t)slot_token(p, win, r) * stb;
   }
   // byte offset of slot r of the unit's window (identity map for full attention)
   __device__ __forceinline__ uint32_t tok(const uint32_t* t, int r) const {

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   const int L = m + p.G;
   const int stok = p.stride_tok;
   if (!FULL) {
-    for (int r = tid; r < m; r += kThreads) sOff[r] = window_token(p.geo, win, r) * stok;
+    for (int r = tid; r < m; r += kThreads) sOff[r] = slot_token(p, win, r) * stok;
     __syncthreads();
   }
   auto tokoff = [&](int r) -> int32_t { return FULL ? r * stok : sOff[r]; };

@@ -457,6 +457,140 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
   }
 }
 
+int basa_hilbert_order(int32_t side, int32_t* order_out) {
+  try {
+    if (!order_out) return fail(BASA_ERR_INVALID_ARG, "order_out must be non-NULL");
+    if (side < 1 || side > (1 << 15) || (side & (side - 1)))
+      return fail(BASA_ERR_INVALID_ARG, "side must be a power of two in [1, 32768] (got %d)", side);
+    // Iterative curve index -> (x, y): each level of two bits picks a quadrant
+    // and rotates/reflects the coordinates accumulated so far.
+    const int64_t n = (int64_t)side * side;
+    for (int64_t d = 0; d < n; ++d) {
+      int64_t t = d, x = 0, y = 0;
+      for (int64_t s = 1; s < side; s *= 2) {
+        const int64_t rx = 1 & (t / 2);
+        const int64_t ry = 1 & (t ^ rx);
+        if (ry == 0) {
+          if (rx == 1) {
+            x = s - 1 - x;
+            y = s - 1 - y;
+          }
+          const int64_t tmp = x;
+          x = y;
+          y = tmp;
+        }
+        x += s * rx;
+        y += s * ry;
+        t /= 4;
+      }
+      order_out[d] = (int32_t)(y * side + x);
+    }
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_hilbert_order");
+  }
+}
+
+int basa_gather_kv(const void* k, const void* v, const int32_t* idx, int64_t n_idx, void* k_out,
+                   void* v_out, int32_t batch, int32_t heads, int32_t head_dim, int64_t n_tokens,
+                   int32_t dtype, int32_t layout, void* stream) {
+  try {
+    if (!k || !v || !idx || !k_out || !v_out)
+      return fail(BASA_ERR_INVALID_ARG, "k, v, idx, k_out and v_out must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    if (n_tokens < 1 || n_idx < 1 || n_idx > (1 << 20))
+      return fail(BASA_ERR_INVALID_ARG, "n_tokens must be >= 1 and n_idx in [1, 2^20]");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out) || (uintptr_t)idx % 4)
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned (idx 4-byte)");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n_tokens, head_dim, &sb, &sh, &stok);
+    if (n_tokens * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "sequence too long for 32-bit token offsets");
+    const size_t es = dtype == BASA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)batch * heads * n_tokens * head_dim * es;
+    const size_t ob = (size_t)batch * heads * n_idx * head_dim * es;
+    if (overlaps(k_out, ob, k, tb) || overlaps(k_out, ob, v, tb) || overlaps(v_out, ob, k, tb) ||
+        overlaps(v_out, ob, v, tb) || overlaps(k_out, ob, v_out, ob) ||
+        overlaps(k_out, ob, idx, n_idx * 4) || overlaps(v_out, ob, idx, n_idx * 4))
+      return fail(BASA_ERR_INVALID_ARG, "an output overlaps an input or the other output");
+    basa::GatherParams p{};
+    p.k = k; p.v = v; p.idx = idx; p.kout = k_out; p.vout = v_out;
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.n = (int32_t)n_tokens; p.n_idx = (int32_t)n_idx;
+    rc = basa::launch_gather(p, dtype, (hipStream_t)stream);
+    if (rc) return fail(rc, "gather launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_gather_kv");
+  }
+}
+
+int basa_curve_attn(const void* q, const void* k, const void* v, const void* k_mem,
+                    const void* v_mem, int64_t n_mem, void* out, int32_t batch, int32_t heads,
+                    int32_t head_dim, int64_t n_tokens, const int32_t* order, int32_t tile,
+                    int64_t slide, float scale, float mem_bias, int32_t dtype, int32_t layout,
+                    void* stream) {
+  try {
+    if (!q || !k || !v || !out || !order)
+      return fail(BASA_ERR_INVALID_ARG, "q, k, v, out and order must be non-NULL");
+    int rc = check_common(batch, heads, head_dim, dtype, layout);
+    if (rc) return rc;
+    if (n_tokens < 1) return fail(BASA_ERR_INVALID_ARG, "n_tokens must be >= 1");
+    if (tile < 1 || n_tokens % tile)
+      return fail(BASA_ERR_INVALID_ARG, "tile (%d) must be positive and divide n_tokens (%lld)", tile, (long long)n_tokens);
+    if (tile > BASA_MAX_WINDOW_TOKENS)
+      return fail(BASA_ERR_UNSUPPORTED, "tile of %d tokens exceeds %d", tile, BASA_MAX_WINDOW_TOKENS);
+    if ((k_mem == nullptr) != (v_mem == nullptr))
+      return fail(BASA_ERR_INVALID_ARG, "k_mem and v_mem must both be given or both be NULL");
+    if (k_mem && (n_mem < 1 || n_mem > (1 << 20)))
+      return fail(BASA_ERR_INVALID_ARG, "n_mem must be in [1, 2^20] with memory (got %lld)", (long long)n_mem);
+    if (!k_mem && n_mem != 0) return fail(BASA_ERR_INVALID_ARG, "n_mem must be 0 without memory");
+    if (not_finite(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
+    if (not_finite(mem_bias)) return fail(BASA_ERR_INVALID_ARG, "mem_bias must be finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (k_mem && (!aligned16(k_mem) || !aligned16(v_mem))) || (uintptr_t)order % 4)
+      return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned (order 4-byte)");
+    int64_t sb, sh, stok;
+    strides(layout, heads, n_tokens, head_dim, &sb, &sh, &stok);
+    if (n_tokens * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "sequence too long for 32-bit token offsets");
+    const size_t es = dtype == BASA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)batch * heads * n_tokens * head_dim * es;
+    const size_t mb = k_mem ? (size_t)batch * heads * n_mem * head_dim * es : 0;
+    if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
+        overlaps(out, tb, k_mem, mb) || overlaps(out, tb, v_mem, mb) ||
+        overlaps(out, tb, order, n_tokens * 4))
+      return fail(BASA_ERR_INVALID_ARG, "out overlaps an input");
+    basa::AttnParams p{};
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.kmem = (const uint16_t*)k_mem; p.vmem = (const uint16_t*)v_mem; p.out = (uint16_t*)out;
+    p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
+    p.m = tile;
+    p.G = k_mem ? (int32_t)n_mem : 0;
+    p.nW = (int32_t)(n_tokens / tile);
+    p.scale = resolve_scale(scale, head_dim);
+    p.c1 = p.scale * basa::kLog2e;
+    p.mem_bias = k_mem ? mem_bias : 0.0f;
+    p.mem_bias_raw = p.mem_bias / p.scale;
+    p.n_tok = (int32_t)n_tokens;
+    p.order = order;
+    p.slide = (int32_t)(((slide % n_tokens) + n_tokens) % n_tokens);
+    // a 1-D grid of nW rows of `tile` tokens; only the window count is read
+    basa::Geometry& geo = p.geo;
+    geo.T = 1; geo.Hg = p.nW; geo.Wg = tile;
+    geo.wt = 1; geo.wy = 1; geo.wx = tile;
+    geo.nwy = p.nW; geo.nwx = 1;
+    rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, false, (hipStream_t)stream)
+                            : basa::launch_attn_f32(p, false, (hipStream_t)stream);
+    if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
+    if (rc) return fail(rc, "curve attention launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_curve_attn");
+  }
+}
+
 int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
                    int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
                    int32_t layout, void* stream) {

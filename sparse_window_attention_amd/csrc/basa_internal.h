@@ -36,8 +36,23 @@ struct AttnParams {
   float mem_bias;         // memory logit bias (natural log units)
   Geometry geo;
   float* lse;             // optional [B*H, n_tok] fp32 natural-log log-sum-exp of every query
-  int32_t n_tok;          // tokens per (batch, head): the lse row length
+  int32_t n_tok;          // tokens per (batch, head)
+  const int32_t* order;   // optional device [n_tok]: a token order whose runs of m
+                          // consecutive positions are the windows (replaces geo)
+  int32_t slide;          // start of window 0 along `order`, in [0, n_tok)
 };
+
+// Raster token of slot r of window `win`: under the shifted grid partition,
+// or, with an explicit token order, position (win*m + slide + r) mod n of
+// that order (entries are clamped into [0, n) so any array is memory-safe).
+__device__ __forceinline__ int32_t slot_token(const AttnParams& p, int32_t win, int32_t r) {
+  if (p.order != nullptr) {
+    const int32_t pos = (int32_t)(((int64_t)win * p.m + p.slide + r) % p.n_tok);
+    const int32_t t = p.order[pos];
+    return t < 0 ? 0 : (t >= p.n_tok ? p.n_tok - 1 : t);
+  }
+  return window_token(p.geo, win, r);
+}
 
 struct PoolParams {
   const void* k;
@@ -86,5 +101,19 @@ int launch_attn_bwd(const BwdParams& p, hipStream_t stream);
 int launch_attn_bf16(const AttnParams& p, bool full, hipStream_t stream);
 int launch_attn_f32(const AttnParams& p, bool full, hipStream_t stream);
 int launch_pool(const PoolParams& p, int dtype, hipStream_t stream);
+
+// Row gather: k_out[bh, i, :] = k[bh, idx[i], :] (same for v), outputs
+// [B*H, n_idx, D] contiguous, indices clamped into [0, n).
+struct GatherParams {
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  void* kout;
+  void* vout;
+  int64_t stride_b, stride_h;
+  int32_t stride_tok;
+  int32_t heads, batch_heads, head_dim, n, n_idx;
+};
+int launch_gather(const GatherParams& p, int dtype, hipStream_t stream);
 
 }  // namespace basa

@@ -126,7 +126,39 @@ int launch_cpr(const PoolParams& p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
+// Row gather for a shared key region (HilbertA catalogue record, abstract: a
+// small central region shared by every tile): one thread per 16-byte chunk.
+__global__ void __launch_bounds__(256) gather_kernel(GatherParams p, int cpr, int es) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.batch_heads * p.n_idx * cpr;
+  if (i >= total) return;
+  const int c = (int)(i % cpr);
+  const int64_t row = i / cpr;                  // bh * n_idx + j
+  const int bh = (int)(row / p.n_idx);
+  const int j = (int)(row - (int64_t)bh * p.n_idx);
+  int t = p.idx[j];
+  t = t < 0 ? 0 : (t >= p.n ? p.n - 1 : t);
+  const int b = bh / p.heads, h = bh - b * p.heads;
+  const int64_t src = ((int64_t)b * p.stride_b + (int64_t)h * p.stride_h + (int64_t)t * p.stride_tok) * es + c * 16;
+  const int64_t dst = row * (int64_t)p.head_dim * es + c * 16;
+  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.kout) + dst) =
+      *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.k) + src);
+  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.vout) + dst) =
+      *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.v) + src);
+}
+
 }  // namespace
+
+int launch_gather(const GatherParams& p, int dtype, hipStream_t stream) {
+  const int es = dtype == BASA_BF16 ? 2 : 4;
+  const int cpr = p.head_dim * es / 16;
+  const int64_t total = (int64_t)p.batch_heads * p.n_idx * cpr;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > INT32_MAX) return BASA_ERR_UNSUPPORTED;
+  if (blocks == 0) return BASA_OK;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, cpr, es);
+  return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
 
 int launch_pool(const PoolParams& p, int dtype, hipStream_t stream) {
   const bool bf16 = dtype == BASA_BF16;

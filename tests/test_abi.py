@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(S.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -222,3 +222,59 @@ def test_fwd_lse_validation():
     assert f(*args, None, *rest, S.BASA_BF16, 0, None) == S.BASA_ERR_INVALID_ARG
     assert f(*args, FAKE + 4 * SZ, *rest, S.BASA_F32, 0, None) == S.BASA_ERR_UNSUPPORTED
     assert f(*args, FAKE + 3 * SZ + 64, *rest, S.BASA_BF16, 0, None) == S.BASA_ERR_INVALID_ARG
+
+
+def test_hilbert_order_validation():
+    buf = (ctypes.c_int32 * 16)()
+    assert S.lib.basa_hilbert_order(4, buf) == S.BASA_OK
+    assert S.lib.basa_hilbert_order(4, None) == S.BASA_ERR_INVALID_ARG
+    for side in (0, 3, 6, 1 << 16):
+        assert S.lib.basa_hilbert_order(side, buf) == S.BASA_ERR_INVALID_ARG
+
+
+def _curve(**kw):
+    a = dict(q=FAKE, k=FAKE + SZ, v=FAKE + 2 * SZ, km=FAKE + 3 * SZ, vm=FAKE + 4 * SZ, G=64,
+             out=FAKE + 5 * SZ, B=1, H=2, D=128, n=4096, order=FAKE + 6 * SZ, tile=256,
+             slide=0, scale=-1.0, bias=0.0, dtype=S.BASA_BF16, layout=S.BASA_LAYOUT_BHND)
+    a.update(kw)
+    return S.lib.basa_curve_attn(a["q"], a["k"], a["v"], a["km"], a["vm"], a["G"], a["out"],
+                                 a["B"], a["H"], a["D"], a["n"], a["order"], a["tile"],
+                                 a["slide"], a["scale"], a["bias"], a["dtype"], a["layout"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(order=None), S.BASA_ERR_INVALID_ARG),
+    (dict(q=None), S.BASA_ERR_INVALID_ARG),
+    (dict(tile=0), S.BASA_ERR_INVALID_ARG),
+    (dict(tile=300), S.BASA_ERR_INVALID_ARG),                     # does not divide n
+    (dict(n=1 << 14, tile=8192), S.BASA_ERR_UNSUPPORTED),         # tile above the maximum
+    (dict(km=None), S.BASA_ERR_INVALID_ARG),                      # one memory operand
+    (dict(km=None, vm=None), S.BASA_ERR_INVALID_ARG),             # n_mem without memory
+    (dict(G=0), S.BASA_ERR_INVALID_ARG),
+    (dict(order=FAKE + 6 * SZ + 2), S.BASA_ERR_INVALID_ARG),      # misaligned order
+    (dict(out=FAKE + 6 * SZ), S.BASA_ERR_INVALID_ARG),            # out overlaps order
+    (dict(out=FAKE + 64), S.BASA_ERR_INVALID_ARG),                # out overlaps q
+    (dict(scale=float("inf")), S.BASA_ERR_INVALID_ARG),
+    (dict(bias=float("nan")), S.BASA_ERR_INVALID_ARG),
+    (dict(D=96), S.BASA_ERR_UNSUPPORTED),
+    (dict(dtype=7), S.BASA_ERR_UNSUPPORTED),
+])
+def test_curve_attn_validation(kw, code):
+    assert _curve(**kw) == code
+    assert len(S.lib.basa_last_error().decode()) > 5
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE + SZ, None, 64, FAKE + 3 * SZ, FAKE + 4 * SZ), S.BASA_ERR_INVALID_ARG),
+    ((FAKE, FAKE + SZ, FAKE + 2 * SZ, 0, FAKE + 3 * SZ, FAKE + 4 * SZ), S.BASA_ERR_INVALID_ARG),
+    ((FAKE, FAKE + SZ, FAKE + 2 * SZ + 1, 64, FAKE + 3 * SZ, FAKE + 4 * SZ),
+     S.BASA_ERR_INVALID_ARG),
+    ((FAKE, FAKE + SZ, FAKE + 2 * SZ, 64, FAKE + 16, FAKE + 4 * SZ), S.BASA_ERR_INVALID_ARG),
+    ((FAKE, FAKE + SZ, FAKE + 2 * SZ, 64, FAKE + 3 * SZ, FAKE + 3 * SZ + 64),
+     S.BASA_ERR_INVALID_ARG),
+])
+def test_gather_kv_validation(args, code):
+    rc = S.lib.basa_gather_kv(*args, 1, 2, 128, 4096, S.BASA_BF16, S.BASA_LAYOUT_BHND, None)
+    assert rc == code
+    assert len(S.lib.basa_last_error().decode()) > 5

@@ -30,6 +30,18 @@ def test_hilbert_side_two_by_definition():
     assert O.hilbert_curve_xy(2) == [(0, 0), (0, 1), (1, 1), (1, 0)]
 
 
+@pytest.mark.parametrize("side", [2, 4, 16, 64, 128])
+def test_library_hilbert_order_matches_oracle(side):
+    S = pytest.importorskip("sparse_window_attention_amd")
+    assert np.array_equal(S.hilbert_order(side), O.hilbert_order(side))
+
+
+def test_library_center_region_matches_oracle():
+    S = pytest.importorskip("sparse_window_attention_amd")
+    for grid, size in [((8, 8), (2, 2)), ((64, 64), (8, 8)), ((10, 12), (3, 4))]:
+        assert np.array_equal(S.center_region_tokens(grid, size), O.center_region(grid, size))
+
+
 @pytest.mark.parametrize("tile,slide,mem", [(16, 0, False), (16, 5, True), (64, 40, True),
                                             (4, 1, False)])
 def test_curve_attention_equals_masked_definition(tile, slide, mem):
