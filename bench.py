@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (vendor figure)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (vendor figure)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_attn_traffic.json")
 KERNEL_SOURCES = ["sparse_window_attention_amd/csrc/attn_bf16.hip",
+                  "sparse_window_attention_amd/csrc/basa_internal.h",
                   "sparse_window_attention_amd/csrc/basa_common.h"]
 
 
