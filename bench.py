@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "hilbert", "all"),
+    ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "hilbert", "calib",
+                                       "all"),
                     default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
                          "at the same shape; 'copy': a plain device copy of known size, the "
@@ -147,6 +148,31 @@ def time_dense(S, sets, reps, stream):
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b))
     return ts
+
+
+def measure_mfma_peak(S, stream, reps=5):
+    """bf16 MFMA rate of the library's calibration loop (no memory traffic),
+    four workgroups of 8 waves per compute unit: the rate the matrix cores
+    sustain on this chip at its clocks under full load."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 4 * cus, 4000
+    sink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+    S.calib_mfma(sink, blocks, 200)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fl = S.calib_mfma(sink, blocks, iters)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = median(ts)
+    return {"tflops": fl / (ms * 1e-3) / 1e12, "ms": ms, "flops": fl, "compute_units": cus,
+            "note": "4 independent 32x32x16 bf16 MFMA chains per wave, 8 waves x 4 workgroups "
+                    "per CU, register operands only"}
 
 
 COPY_BYTES = 1 << 30   # bytes read (and again written) by one calibration copy
@@ -550,6 +576,9 @@ def main():
         sets = make_sets(head, 2, dev)
         print(json.dumps(measure_backward(S, head, sets, args.steps, stream)))
         return
+    if args.only == "calib":
+        print(json.dumps(measure_mfma_peak(S, stream)))
+        return
     if args.only == "hilbert":
         print(json.dumps(measure_hilbert(S, stream, dev, args.steps)))
         return
@@ -597,10 +626,13 @@ def main():
         roof = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "attn_bf16_persistent_kernel<128,false,8,64>"
+    roof["kernel"] = "attn_bf16_persistent_kernel<128,false,8,64,true>"
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = byts
     roof["mfma_frac"] = res["window_attn_mfma_frac"]
+    calib = measure_mfma_peak(S, stream)
+    roof["measured_mfma_peak_tflops"] = calib["tflops"]
+    roof["frac_of_measured_mfma_peak"] = flops / t / 1e12 / calib["tflops"]
     roof["kernel_source_hash"] = kernel_hash()
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -631,6 +663,7 @@ def main():
         "composition_baseline": comp,
         "backward": bwd,
         "hilbert_tiles": hil,
+        "mfma_calibration": calib,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -265,6 +265,19 @@ int basa_curve_attn(const void* q, const void* k, const void* v,
                     void* stream);
 
 /*
+ * Calibration, not part of the method: runs the library's bf16 MFMA loop
+ * (four independent chains of 32x32x16 products per wave, no memory
+ * traffic) over `blocks` workgroups of 8 waves, `iters` iterations each, so a
+ * caller can time the matrix-core rate the chip sustains and use it beside
+ * the vendor's dense peak as a roofline denominator.  Work per call:
+ * blocks * 8 * iters * 4 * 32768 flops.
+ *   sink    device float [blocks], receives one value per workgroup
+ *   blocks  >= 1; iters >= 1
+ * Errors: INVALID_ARG (NULL sink, sizes), HIP (launch).
+ */
+int basa_calib_mfma(float* sink, int32_t blocks, int32_t iters, void* stream);
+
+/*
  * Dense full attention out = softmax(scale * q k^T) v over all n_tokens keys
  * per (batch, head) [BASA-2 complexity paragraph: the O(n^2) cost that window
  * attention reduces to O(n*m)].  Built only to measure realised against

@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
                                                 i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
         "basa_window_attn_bwd_workspace": (i64, [i32, i32, i32, i32, pi32, pi32]),
         "basa_hilbert_order": (ctypes.c_int, [i32, pi32]),
+        "basa_calib_mfma": (ctypes.c_int, [vp, i32, i32, vp]),
         "basa_gather_kv": (ctypes.c_int, [vp, vp, vp, i64, vp, vp, i32, i32, i32, i64, i32, i32,
                                           vp]),
         "basa_curve_attn": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, i32, i32, i32, i64, vp,
@@ -309,6 +310,17 @@ def window_attn_bwd(q, k, v, out, dout, lse, grid: Sequence[int], window: Sequen
         _arr(window), _arr(shift), None if pool is None else _arr(pool), s, float(mem_bias),
         _dtype_code(q), lay, _stream(q)))
     return dq, dk, dv
+
+
+def calib_mfma(sink, blocks: int, iters: int):
+    """Runs the bf16 MFMA calibration loop (blocks x 8 waves x iters x 4
+    products of 32768 flops) on the current stream; returns its flop count.
+    ``sink`` is a float32 GPU tensor of at least ``blocks`` elements."""
+    torch = _torch()
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks:
+        raise ValueError("sink must be a float32 GPU tensor of at least `blocks` elements")
+    _check(lib.basa_calib_mfma(sink.data_ptr(), int(blocks), int(iters), _stream(sink)))
+    return int(blocks) * 8 * int(iters) * 4 * 32768
 
 
 def full_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "bhnd"):

@@ -255,6 +255,108 @@ struct Core {
     }
   }
 
+  // ---- direct global-to-LDS tile path (persistent kernel).  A K or V tile
+  // is kKT rows of D bf16, stored row-major without padding by 1 KB
+  // buffer-to-LDS loads (64 lanes x 16 bytes each).  The 16-byte chunks of
+  // every row are permuted by an XOR with a function of the row, chosen so
+  // that the operand reads below spread over all LDS banks: for K, the 16
+  // rows read by a quarter wave land in 16 distinct chunk slots; for V, the
+  // 4 rows x 4 chunks read by a half wave do.  The chunk a lane fetches from
+  // global memory is the one its fixed LDS slot must hold.
+  static constexpr int kTileB = kKT * D * 2;    // bytes of one K or V tile
+  static constexpr int RPB = 16 / TL::CPR;      // rows per 256 bytes
+  static constexpr int kDmaIns = kTileB / 1024; // load instructions per tile
+  static constexpr int kDmaIpw = kDmaIns / NW;  // per wave
+  static_assert(kDmaIpw >= 1 && kDmaIpw * NW == kDmaIns, "tile must split over the waves");
+  __device__ static __forceinline__ int swz_k(int r) { return (r / RPB) & (TL::CPR - 1); }
+  __device__ static __forceinline__ int swz_v(int r) { return (4 * (r / RPB)) & (TL::CPR - 4); }
+
+  // Issues this wave's share of the loads of tile `tile` (K or V) into `buf`.
+  __device__ __forceinline__ void dma_tile(unsigned char* buf, const Unit& u, const uint32_t* t,
+                                           int tile, bool isv) const {
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int k0 = tile * kKT;
+#pragma unroll
+    for (int i = 0; i < kDmaIpw; ++i) {
+      const int ins = wv * kDmaIpw + i;
+      const int r = (ins * 64 + lane) / TL::CPR;
+      const uint32_t cb = (uint32_t)(((lane % TL::CPR) ^ (isv ? swz_v(r) : swz_k(r))) * 16);
+      auto* lds = (__attribute__((address_space(3))) void*)(buf + ins * 1024);
+      if constexpr (FULL) {
+        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, (uint32_t)min(k0 + r, L - 1) * stb + cb,
+                                                 0, 0, 0);
+      } else if (k0 + kKT <= m) {
+        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, t[k0 + r] + cb, 0, 0, 0);
+      } else if (k0 >= m && k0 + kKT <= L) {
+        const Rsrc rs = make_rsrc((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, (uint32_t)r * (D * 2) + cb,
+                                                 (uint32_t)(k0 - m) * (D * 2), 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(row_ptr(u, t, k0 + r, isv) + cb), lds,
+            16, 0, 0);
+      }
+    }
+  }
+  // S^T = K Q^T with K from a swizzled tile.  Row kb*32 + l32 has the
+  // swizzle x of row l32 (32 rows span whole swizzle periods); chunk
+  // hf*CPR/2 + ss sits at slot (hf*CPR/2 + ss) ^ x, so the byte offset is one
+  // lane base XOR 16*ss, and kb and the buffer are immediate offsets.
+  __device__ __forceinline__ void compute_s_dma(const unsigned char* kt, Scores& s) const {
+    const f32x16 zero16 = {};
+    constexpr int H = TL::CPR / 2;
+    const int x = swz_k(l32);
+    const uint32_t kbase = (uint32_t)(l32 * (TL::CPR * 16) + 16 * ((hf * H) ^ (x & H)) + 16 * (x & (H - 1)));
+#pragma unroll
+    for (int ss = 0; ss < QS; ++ss) {
+      const uint32_t off = kbase ^ (uint32_t)(16 * ss);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + off + kb * 32 * (TL::CPR * 16));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qreg[qb][ss]),
+              ss == 0 ? zero16 : s[qb][kb], 0, 0, 0);
+      }
+    }
+  }
+  // O^T += V^T P^T with V^T read from the row-major tile by transposing LDS
+  // reads.  One read gives lane i of each 16-lane group element j of the row
+  // read by lane 4j + i/4 of its group, column i%4 of that lane's 4 values;
+  // the addresses below make lane l receive, for the operand's k index
+  // 8*hf + 4*h + j, the key 16*sl + 8*h + 4*hf + j at column d = 32*db + l%32,
+  // the key order the P operand takes from the score accumulators.  The
+  // swizzle of such a key depends only on j, so each d block has one lane
+  // base and (sl, h) are immediate offsets.
+  __device__ __forceinline__ void pv_dma(const unsigned char* vt, const Probs& pb) {
+    const int lane = tid & 63;
+    const int sq = (lane & 15) >> 2;       // row within the 4-row group
+    const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
+    const uint32_t lanev = (uint32_t)((4 * hf + sq) * (TL::CPR * 16) + (d0 & 7) * 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t vb = lanev + (uint32_t)((((4 * db + (d0 >> 3)) ^ swz_v(sq)) * 16));
+#pragma unroll
+      for (int sl = 0; sl < 2 * KB; ++sl) {
+        bf16x4 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
+              vt + vb + (16 * sl + 8 * h) * (TL::CPR * 16)));
+        const bf16x8 av = {h2[0][0], h2[0][1], h2[0][2], h2[0][3],
+                           h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              av, __builtin_bit_cast(bf16x8, pb[qb][sl]), acc[qb][db], 0, 0, 0);
+      }
+    }
+  }
+
   // ---- query rows of block qb: row wave*kQPW + 32*qb + l32 of the unit
   __device__ __forceinline__ int qrow(const Unit& u, int qb) const {
     return u.qt * TL::kQT + wave * TL::kQPW + 32 * qb + l32;
@@ -551,9 +653,12 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // LDS of the persistent kernel: the tile buffers, two window tables (the
 // current unit's and the next one's) and, per wave, a staging area for the
 // next unit's Q rows, filled by direct global-to-LDS loads.
-template <int D, bool FULL, int NW, int KT>
+template <int D, bool FULL, int NW, int KT, bool DMA>
 struct PersistLayout {
   using TL = Tiles<D, NW, 1, KT>;
+  // two K and two V tile buffers: padded K and transposed V, or (DMA) four
+  // row-major swizzled tiles
+  static constexpr int tileBytes = DMA ? 4 * KT * D * 2 : TL::tileBytes;
   static constexpr int CPR = D / 8;        // 16B chunks per Q row
   static constexpr int RPI = 64 / CPR;     // Q rows per load instruction (64 lanes x 16B)
   static constexpr int QI = 32 / RPI;      // instructions per wave and unit
@@ -562,7 +667,7 @@ struct PersistLayout {
     return FULL ? 0 : ((size_t)m * 4 + 15) / 16 * 16;
   }
   __host__ __device__ static constexpr size_t stage_offset(int m) {
-    return TL::tileBytes + 2 * table_bytes(m);
+    return tileBytes + 2 * table_bytes(m);
   }
   __host__ __device__ static constexpr size_t bytes(int m) {
     return stage_offset(m) + (size_t)NW * kQWave;
@@ -577,11 +682,11 @@ struct PersistLayout {
 // tile nkt+1, and its Q rows once the current unit's last scores are formed.
 // The tile count is rounded up to an even number (a padding tile has only
 // masked keys), so tile t of every unit uses buffer t & 1.
-template <int D, bool FULL, int NW, int KT>
+template <int D, bool FULL, int NW, int KT, bool DMA>
 __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnParams p) {
   using C = Core<D, FULL, NW, 1, KT>;
   using TL = typename C::TL;
-  using PL = PersistLayout<D, FULL, NW, KT>;
+  using PL = PersistLayout<D, FULL, NW, KT, DMA>;
   constexpr int kKT = KT;
   using Scores = typename C::Scores;
   using Probs = typename C::Probs;
@@ -600,7 +705,22 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
   // even tile count; a padding tile holds only keys >= L, which the mask removes
   const int nkt = (c.nkt + 1) & ~1;
   if (nkt != c.nkt) c.tmask = min(c.tmask, c.nkt);
-  unsigned char* tables = smem + TL::tileBytes;
+  unsigned char* tables = smem + PL::tileBytes;
+  // DMA tile buffers: K buffer b at b * kTileB, V buffer b at (2 + b) * kTileB
+  auto dK = [&](int b) __attribute__((always_inline)) { return smem + b * C::kTileB; };
+  auto dV = [&](int b) __attribute__((always_inline)) { return smem + (2 + b) * C::kTileB; };
+  auto get_v = [&](const Unit& u, const uint32_t* tb, int tile) __attribute__((always_inline)) {
+    if constexpr (DMA) c.dma_tile(dV(tile & 1), u, tb, tile, true);
+    else c.load_v(u, tb, tile);
+  };
+  auto get_k = [&](const Unit& u, const uint32_t* tb, int tile) __attribute__((always_inline)) {
+    if constexpr (DMA) c.dma_tile(dK(tile & 1), u, tb, tile, false);
+    else c.load_k(u, tb, tile);
+  };
+  auto scores = [&](int b, Scores& sc) __attribute__((always_inline)) {
+    if constexpr (DMA) c.compute_s_dma(dK(b), sc);
+    else c.compute_s(c.sK(b), sc);
+  };
   auto tab_of = [&](int j) __attribute__((always_inline)) {
     return reinterpret_cast<uint32_t*>(tables + (j & 1) * PL::table_bytes(c.m));
   };
@@ -651,7 +771,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
     lds_barrier();
   }
   load_q_of(uc, tab_of(0));
-  {
+  if constexpr (DMA) {
+    get_k(uc, tab_of(0), 0);
+    get_v(uc, tab_of(0), 0);
+    get_k(uc, tab_of(0), 1);
+    wait_vmem();
+  } else {
     u32x4 k1[TL::KPASS];
     c.load_k(uc, tab_of(0), 0);
     c.load_v(uc, tab_of(0), 0);
@@ -662,7 +787,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
   }
   lds_barrier();  // tiles 0 and 1 of unit 0 are in LDS
   Scores sA, sB;
-  c.compute_s(c.sK(0), sA);
+  scores(0, sA);
   auto copy = [&](Scores& dst, const Scores& src) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) dst[0][kb] = src[0][kb];
@@ -685,12 +810,20 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
       c.rowmax_all(sA, mx);
       c.update_max(mx);
     }
-    c.load_v(uc, tab, 1);
-    c.load_k(uc, tab, 2);
+    if constexpr (!DMA) {
+      c.load_v(uc, tab, 1);
+      c.load_k(uc, tab, 2);
+    }
     // Every wave is done with K(0) (and with the previous unit's output
     // rows, read through its table) before iteration 0 refills the buffer
-    // and the next unit's table overwrites the previous unit's.
+    // and the next unit's table overwrites the previous unit's.  Direct
+    // loads into LDS go out only after this barrier: until then other waves
+    // may still read the buffers (the previous unit's last V tile).
     lds_barrier();
+    if constexpr (DMA) {
+      get_v(uc, tab, 1);
+      get_k(uc, tab, 2);
+    }
     if (!FULL && j >= 1 && has_next) c.build_table(tab_of(j + 1), un.win);
 
     // Iteration t: as in the unit kernel; the loads past the unit's last tile
@@ -698,24 +831,29 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
     auto iter = [&](int t, Scores& sc, Scores& sn, auto masked) __attribute__((always_inline)) {
       Probs pb;
       float mxn[1];
-      c.compute_s(c.sK((t + 1) & 1), sn);
+      scores((t + 1) & 1, sn);
       c.make_p(sc, pb);
-      c.pv(c.sV(t & 1), pb);
+      if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
+      else c.pv(c.sV(t & 1), pb);
       if constexpr (decltype(masked)::value) c.mask_s(sn, (t + 1) * kKT);
       c.rowmax_all(sn, mxn);
-      c.store_v((t + 1) & 1);
-      c.store_k(t & 1);
+      if constexpr (DMA) {
+        wait_vmem();  // this wave's loads of V(t+1) and K(t+2)
+      } else {
+        c.store_v((t + 1) & 1);
+        c.store_k(t & 1);
+      }
       lds_barrier();
       const int tv = t + 2, tk = t + 3;
       if (tv < nkt || (has_next && tv == nkt)) {
         const bool cur = tv < nkt;
         const Unit u = cur ? uc : un;  // by value: the choice stays in registers
-        c.load_v(u, cur ? tab : tabn, cur ? tv : 0);
+        get_v(u, cur ? tab : tabn, cur ? tv : 0);
       }
       if (tk < nkt || (has_next && tk <= nkt + 1)) {
         const bool cur = tk < nkt;
         const Unit u = cur ? uc : un;
-        c.load_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
+        get_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
       }
       if (has_next && t < qstep)
         for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
@@ -743,7 +881,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
     {
       Probs pb;
       c.make_p(sA, pb);
-      c.pv(c.sV(t & 1), pb);
+      if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
+      else c.pv(c.sV(t & 1), pb);
     }
     if (!has_next) {
       finish_of(uc, tab);
@@ -758,9 +897,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
     // covers those stores.
     wait_vmem();
     unstage_q();
-    c.store_v(0);
-    c.store_k(1);
-    c.compute_s(c.sK(0), sA);
+    if constexpr (!DMA) {
+      c.store_v(0);
+      c.store_k(1);
+    }
+    scores(0, sA);
     finish_of(uc, tab);
     uc = un;
     un = unit_at(j + 2);
@@ -783,6 +924,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
 #endif
 #ifndef BASA_PERSISTENT_KTILE
 #define BASA_PERSISTENT_KTILE 64
+#endif
+// K/V tiles of the persistent kernel by direct buffer-to-LDS loads (swizzled,
+// V^T read with transposing LDS reads) instead of through registers.
+#ifndef BASA_PERSISTENT_DMA
+#define BASA_PERSISTENT_DMA 1
 #endif
 template <typename K>
 int set_lds_limit(K kernel, bool& done) {
@@ -823,18 +969,19 @@ inline int set_units(AttnParams& p, int kQT) {
 // -1 (nothing launched) otherwise.
 template <int D, bool FULL, int NW, int KT>
 int launch_persistent(const AttnParams& p0, hipStream_t stream) {
+  constexpr bool DMA = BASA_PERSISTENT_DMA != 0;
   using TL = Tiles<D, NW, 1, KT>;
-  using SL = PersistLayout<D, FULL, NW, KT>;
+  using SL = PersistLayout<D, FULL, NW, KT, DMA>;
   const int nkt = (p0.m + p0.G + KT - 1) / KT;
   const size_t lds = SL::bytes(p0.m);
   if (nkt < kPersistentMinTiles || lds > 160 * 1024) return -1;
   AttnParams p = p0;
   if (int e = set_units(p, TL::kQT)) return e;
   static bool attr = false;
-  if (set_lds_limit(&attn_bf16_persistent_kernel<D, FULL, NW, KT>, attr)) return BASA_ERR_HIP;
+  if (set_lds_limit(&attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>, attr)) return BASA_ERR_HIP;
   const int per_xcd = max(1, min(p.units_per_xcd, cu_count() / 8));
-  hipLaunchKernelGGL((attn_bf16_persistent_kernel<D, FULL, NW, KT>), dim3((unsigned)(8 * per_xcd)),
-                     dim3(TL::kThreads), lds, stream, p);
+  hipLaunchKernelGGL((attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>),
+                     dim3((unsigned)(8 * per_xcd)), dim3(TL::kThreads), lds, stream, p);
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 

@@ -591,6 +591,18 @@ int basa_curve_attn(const void* q, const void* k, const void* v, const void* k_m
   }
 }
 
+int basa_calib_mfma(float* sink, int32_t blocks, int32_t iters, void* stream) {
+  try {
+    if (!sink) return fail(BASA_ERR_INVALID_ARG, "sink must be non-NULL");
+    if (blocks < 1 || iters < 1) return fail(BASA_ERR_INVALID_ARG, "blocks and iters must be >= 1");
+    const int rc = basa::launch_mfma_rate(sink, blocks, iters, (hipStream_t)stream);
+    if (rc) return fail(rc, "calibration launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_calib_mfma");
+  }
+}
+
 int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
                    int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
                    int32_t layout, void* stream) {

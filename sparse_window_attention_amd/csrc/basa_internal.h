@@ -115,5 +115,7 @@ struct GatherParams {
   int32_t heads, batch_heads, head_dim, n, n_idx;
 };
 int launch_gather(const GatherParams& p, int dtype, hipStream_t stream);
+// Calibration: the bf16 MFMA loop of calib.hip over `blocks` workgroups.
+int launch_mfma_rate(float* sink, int blocks, int iters, hipStream_t stream);
 
 }  // namespace basa

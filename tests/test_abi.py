@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(S.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -278,3 +278,9 @@ def test_gather_kv_validation(args, code):
     rc = S.lib.basa_gather_kv(*args, 1, 2, 128, 4096, S.BASA_BF16, S.BASA_LAYOUT_BHND, None)
     assert rc == code
     assert len(S.lib.basa_last_error().decode()) > 5
+
+
+def test_calib_mfma_validation():
+    assert S.lib.basa_calib_mfma(None, 4, 10, None) == S.BASA_ERR_INVALID_ARG
+    assert S.lib.basa_calib_mfma(FAKE, 0, 10, None) == S.BASA_ERR_INVALID_ARG
+    assert S.lib.basa_calib_mfma(FAKE, 4, 0, None) == S.BASA_ERR_INVALID_ARG
