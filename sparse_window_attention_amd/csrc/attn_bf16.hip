@@ -44,6 +44,18 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
 constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel needs
+// Persistent kernel: waves per workgroup and workgroups per CU.
+#ifndef BASA_PERSISTENT_WAVES
+#define BASA_PERSISTENT_WAVES 8
+#endif
+#ifndef BASA_PERSISTENT_WGS
+#define BASA_PERSISTENT_WGS 1
+#endif
+// Persistent kernel: stage the next unit's Q rows in LDS (1) or load them
+// into registers at the unit boundary (0).
+#ifndef BASA_PERSISTENT_QSTAGE
+#define BASA_PERSISTENT_QSTAGE 1
+#endif
 
 template <int D, int NW, int QB, int KT>
 struct Tiles {
@@ -670,7 +682,7 @@ struct PersistLayout {
     return tileBytes + 2 * table_bytes(m);
   }
   __host__ __device__ static constexpr size_t bytes(int m) {
-    return stage_offset(m) + (size_t)NW * kQWave;
+    return stage_offset(m) + (BASA_PERSISTENT_QSTAGE ? (size_t)NW * kQWave : 0);
   }
 };
 
@@ -683,7 +695,7 @@ struct PersistLayout {
 // The tile count is rounded up to an even number (a padding tile has only
 // masked keys), so tile t of every unit uses buffer t & 1.
 template <int D, bool FULL, int NW, int KT, bool DMA>
-__global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnParams p) {
+__global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persistent_kernel(AttnParams p) {
   using C = Core<D, FULL, NW, 1, KT>;
   using TL = typename C::TL;
   using PL = PersistLayout<D, FULL, NW, KT, DMA>;
@@ -856,7 +868,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
         get_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
       }
       if (has_next && t < qstep)
-        for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
+        if constexpr (BASA_PERSISTENT_QSTAGE) {
+          for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
+        }
       c.update_max(mxn);
     };
     int t = 0;
@@ -896,7 +910,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_persistent_kernel(AttnPa
     // before this unit's output stores are issued, so no wait for a load
     // covers those stores.
     wait_vmem();
-    unstage_q();
+    if constexpr (BASA_PERSISTENT_QSTAGE) unstage_q();
+    else load_q_of(un, tabn);
     if constexpr (!DMA) {
       c.store_v(0);
       c.store_k(1);
@@ -974,12 +989,12 @@ int launch_persistent(const AttnParams& p0, hipStream_t stream) {
   using SL = PersistLayout<D, FULL, NW, KT, DMA>;
   const int nkt = (p0.m + p0.G + KT - 1) / KT;
   const size_t lds = SL::bytes(p0.m);
-  if (nkt < kPersistentMinTiles || lds > 160 * 1024) return -1;
+  if (nkt < kPersistentMinTiles || lds * BASA_PERSISTENT_WGS > 160 * 1024) return -1;
   AttnParams p = p0;
   if (int e = set_units(p, TL::kQT)) return e;
   static bool attr = false;
   if (set_lds_limit(&attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>, attr)) return BASA_ERR_HIP;
-  const int per_xcd = max(1, min(p.units_per_xcd, cu_count() / 8));
+  const int per_xcd = max(1, min(p.units_per_xcd, BASA_PERSISTENT_WGS * cu_count() / 8));
   hipLaunchKernelGGL((attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>),
                      dim3((unsigned)(8 * per_xcd)), dim3(TL::kThreads), lds, stream, p);
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
@@ -1005,7 +1020,7 @@ int launch_full_or_window(const AttnParams& p, hipStream_t stream) {
   constexpr int KT = (D == 64 && BASA_ATTN_KTILE * D < 64 * 64) ? 64 : BASA_ATTN_KTILE;
   constexpr int KTS = (D == 64 && BASA_PERSISTENT_KTILE * D < 64 * 64) ? 64 : BASA_PERSISTENT_KTILE;
 #if BASA_PERSISTENT
-  const int e = launch_persistent<D, FULL, BASA_ATTN_WAVES, KTS>(p, stream);
+  const int e = launch_persistent<D, FULL, BASA_PERSISTENT_WAVES, KTS>(p, stream);
   if (e >= 0) return e;
 #endif
   return launch_unit<D, FULL, BASA_ATTN_WAVES, BASA_ATTN_QBLOCKS, KT>(p, stream);

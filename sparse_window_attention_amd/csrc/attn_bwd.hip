@@ -265,13 +265,28 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- dk, dv
 // MEM: memory-key units (b*h, memory chunk of 256 keys, query chunk) writing
 // fp32 partials; otherwise window-key units (b*h, window, key chunk of 256)
-// writing the final gradients.  PASS 0: dV; PASS 1: dK.
+// writing the final gradients.  PASS 0: dV; PASS 1: dK.  Each iteration
+// stages kSub blocks of 32 queries (one barrier per kSub blocks) and works
+// through them one after another, so the products of one block can overlap
+// the exponentials of the next.
+constexpr int kSub = 2;
+
+template <int D, int PASS>
+struct DkdvLayout {
+  using T = BT<D>;
+  // per 32-query block: Q rows, then pass 0: dO^T; pass 1: dO rows and Q^T;
+  // then lse and Dv (32 floats each)
+  static constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
+  static constexpr int kBlock = kMain + 2 * 32 * 4;
+  static constexpr int kBuf = kSub * kBlock;     // one staging buffer
+};
+
 template <int D, bool MEM, int PASS>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   using T = BT<D>;
-  // buffer: Q rows, then pass 0: dO^T; pass 1: dO rows and Q^T; then lse, Dv
-  constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
-  constexpr int kBuf = kMain + 2 * 32 * 4;
+  using DL = DkdvLayout<D, PASS>;
+  constexpr int kMain = DL::kMain;
+  constexpr int kBuf = DL::kBuf;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int bh, kbase, nq, qbase = 0, win = 0;
   if constexpr (MEM) {
@@ -324,23 +339,27 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
 
-  const int nqb = (nq + kBlk - 1) / kBlk;
+  constexpr int kIter = kSub * kBlk;   // queries per iteration
+  const int nit = (nq + kIter - 1) / kIter;
   const int lr = tid / T::CPR, lc = tid % T::CPR;
   const bool loader = lr < kBlk;
-  u32x4 qx{}, dx{};
+  u32x4 qx[kSub], dx[kSub];
   float lx = INFINITY, dvx = 0.0f;
   auto token_of = [&](int q) __attribute__((always_inline)) {
     return MEM ? qbase + q : tab[q];
   };
-  auto load_block = [&](int blk) __attribute__((always_inline)) {
+  auto load_block = [&](int it) __attribute__((always_inline)) {
     if (loader) {
-      const int q = min(blk * kBlk + lr, nq - 1);
-      const uint32_t off = (uint32_t)token_of(q) * stb + lc * 16;
-      qx = buf_load16(make_rsrc(p.q + base), off, 0);
-      dx = buf_load16(make_rsrc(p.dout + base), off, 0);
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) {
+        const int q = min(it * kIter + sb * kBlk + lr, nq - 1);
+        const uint32_t off = (uint32_t)token_of(q) * stb + lc * 16;
+        qx[sb] = buf_load16(make_rsrc(p.q + base), off, 0);
+        dx[sb] = buf_load16(make_rsrc(p.dout + base), off, 0);
+      }
     }
-    if (tid < kBlk) {
-      const int q = blk * kBlk + tid;
+    if (tid < kIter) {
+      const int q = it * kIter + tid;
       const bool ok = q < nq;
       const int64_t idx = (int64_t)bh * p.n + token_of(ok ? q : nq - 1);
       lx = ok ? p.lse[idx] * kLog2e : INFINITY;   // a missing query gets P = 0
@@ -348,22 +367,25 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto store_block = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* b = smem + buf * kBuf;
-    uint16_t* sq = reinterpret_cast<uint16_t*>(b);
+    unsigned char* bb = smem + buf * kBuf;
     if (loader) {
-      *reinterpret_cast<u32x4*>(sq + lr * T::KS + lc * 8) = qx;
-      if constexpr (PASS == 0) {
-        store_tr<T::TS>(sq + kBlk * T::KS, lr, lc * 8, dx);          // dO^T
-      } else {
-        uint16_t* sdo = sq + kBlk * T::KS;
-        *reinterpret_cast<u32x4*>(sdo + lr * T::KS + lc * 8) = dx;   // dO rows
-        store_tr<T::TS>(sdo + kBlk * T::KS, lr, lc * 8, qx);         // Q^T
+#pragma unroll
+      for (int sb = 0; sb < kSub; ++sb) {
+        uint16_t* sq = reinterpret_cast<uint16_t*>(bb + sb * DL::kBlock);
+        *reinterpret_cast<u32x4*>(sq + lr * T::KS + lc * 8) = qx[sb];
+        if constexpr (PASS == 0) {
+          store_tr<T::TS>(sq + kBlk * T::KS, lr, lc * 8, dx[sb]);          // dO^T
+        } else {
+          uint16_t* sdo = sq + kBlk * T::KS;
+          *reinterpret_cast<u32x4*>(sdo + lr * T::KS + lc * 8) = dx[sb];   // dO rows
+          store_tr<T::TS>(sdo + kBlk * T::KS, lr, lc * 8, qx[sb]);         // Q^T
+        }
       }
     }
-    if (tid < kBlk) {
-      float* sl = reinterpret_cast<float*>(b + kMain);
-      sl[perm32(tid)] = lx;
-      sl[32 + perm32(tid)] = dvx;
+    if (tid < kIter) {
+      float* sl = reinterpret_cast<float*>(bb + (tid / kBlk) * DL::kBlock + kMain);
+      sl[perm32(tid % kBlk)] = lx;
+      sl[32 + perm32(tid % kBlk)] = dvx;
     }
   };
   load_block(0);
@@ -371,69 +393,72 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
   const float c1 = p.c1;
   const float bias = MEM ? p.mem_bias_raw : 0.0f;
-  for (int blk = 0; blk < nqb; ++blk) {
-    if (blk + 1 < nqb) load_block(blk + 1);
-    const unsigned char* b = smem + (blk & 1) * kBuf;
-    const uint16_t* sq = reinterpret_cast<const uint16_t*>(b);
-    const float* sl = reinterpret_cast<const float*>(b + kMain);
-    f32x16 s{};
+  for (int it = 0; it < nit; ++it) {
+    if (it + 1 < nit) load_block(it + 1);
 #pragma unroll
-    for (int ss = 0; ss < T::QS; ++ss) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sq + l32 * T::KS + hf * (D / 2) + ss * 8);
-      s = mfma(a, kreg[ss], s);
-    }
-    float pr[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + hf * 16 + r4 * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i] + bias, c1, -l4[i]));
-    }
-    if constexpr (PASS == 0) {
-      const uint16_t* sdt = sq + kBlk * T::KS;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pb{pack_bf16x2(pr[8 * u], pr[8 * u + 1]), pack_bf16x2(pr[8 * u + 2], pr[8 * u + 3]),
-                       pack_bf16x2(pr[8 * u + 4], pr[8 * u + 5]),
-                       pack_bf16x2(pr[8 * u + 6], pr[8 * u + 7])};
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(sdt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-          acc[db] = mfma(a, pb, acc[db]);
-        }
-      }
-    } else {
-      const uint16_t* sdo = sq + kBlk * T::KS;
-      const uint16_t* sqt = sdo + kBlk * T::KS;
-      f32x16 dp{};
+    for (int sb = 0; sb < kSub; ++sb) {
+      const unsigned char* b = smem + (it & 1) * kBuf + sb * DL::kBlock;
+      const uint16_t* sq = reinterpret_cast<const uint16_t*>(b);
+      const float* sl = reinterpret_cast<const float*>(b + kMain);
+      f32x16 s{};
 #pragma unroll
       for (int ss = 0; ss < T::QS; ++ss) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sdo + l32 * T::KS + hf * (D / 2) + ss * 8);
-        dp = mfma(a, vreg[ss], dp);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sq + l32 * T::KS + hf * (D / 2) + ss * 8);
+        s = mfma(a, kreg[ss], s);
       }
-      float ds[16];
+      float pr[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + hf * 16 + r4 * 4);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + hf * 16 + r4 * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ds[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+        for (int i = 0; i < 4; ++i)
+          pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i] + bias, c1, -l4[i]));
       }
+      if constexpr (PASS == 0) {
+        const uint16_t* sdt = sq + kBlk * T::KS;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pb{pack_bf16x2(ds[8 * u], ds[8 * u + 1]), pack_bf16x2(ds[8 * u + 2], ds[8 * u + 3]),
-                       pack_bf16x2(ds[8 * u + 4], ds[8 * u + 5]),
-                       pack_bf16x2(ds[8 * u + 6], ds[8 * u + 7])};
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 pb{pack_bf16x2(pr[8 * u], pr[8 * u + 1]), pack_bf16x2(pr[8 * u + 2], pr[8 * u + 3]),
+                         pack_bf16x2(pr[8 * u + 4], pr[8 * u + 5]),
+                         pack_bf16x2(pr[8 * u + 6], pr[8 * u + 7])};
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(sqt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-          acc[db] = mfma(a, pb, acc[db]);
+          for (int db = 0; db < T::DB; ++db) {
+            const u32x4 a =
+                *reinterpret_cast<const u32x4*>(sdt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+            acc[db] = mfma(a, pb, acc[db]);
+          }
+        }
+      } else {
+        const uint16_t* sdo = sq + kBlk * T::KS;
+        const uint16_t* sqt = sdo + kBlk * T::KS;
+        f32x16 dp{};
+#pragma unroll
+        for (int ss = 0; ss < T::QS; ++ss) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sdo + l32 * T::KS + hf * (D / 2) + ss * 8);
+          dp = mfma(a, vreg[ss], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + hf * 16 + r4 * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 pb{pack_bf16x2(ds[8 * u], ds[8 * u + 1]), pack_bf16x2(ds[8 * u + 2], ds[8 * u + 3]),
+                         pack_bf16x2(ds[8 * u + 4], ds[8 * u + 5]),
+                         pack_bf16x2(ds[8 * u + 6], ds[8 * u + 7])};
+#pragma unroll
+          for (int db = 0; db < T::DB; ++db) {
+            const u32x4 a =
+                *reinterpret_cast<const u32x4*>(sqt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+            acc[db] = mfma(a, pb, acc[db]);
+          }
         }
       }
     }
-    if (blk + 1 < nqb) store_block((blk + 1) & 1);
+    if (it + 1 < nit) store_block((it + 1) & 1);
     __syncthreads();
   }
 
@@ -492,9 +517,7 @@ int set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MEM, int PASS>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
-  using T = BT<D>;
-  constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
-  const size_t lds = 2 * (kMain + 2 * 32 * 4) + (MEM ? 0 : (size_t)p.m * 4);
+  const size_t lds = 2 * (size_t)DkdvLayout<D, PASS>::kBuf + (MEM ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
   const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + kUnit - 1) / kUnit) * p.nqc
                             : (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
