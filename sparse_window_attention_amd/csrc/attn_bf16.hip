@@ -19,13 +19,16 @@
 // t.  K runs one tile ahead of V through two LDS buffers each.
 //
 // Two kernels share this core.  The unit kernel runs one workgroup per work
-// unit.  The persistent kernel (used when a unit has at least
-// kPersistentMinTiles tiles and its LDS fits) runs one workgroup per CU that
-// walks a list of units of one XCD with the same tile loop.  While a unit
-// runs, the next unit's Q rows and first three K/V tiles are copied into an
-// LDS staging area by direct global-to-LDS loads spread over the iterations,
-// so the next unit starts from LDS instead of paying a burst of HBM loads,
-// and the finished unit's output stores drain while the next one computes.
+// unit and stages tiles through registers (V written transposed).  The
+// persistent kernel (used when a unit has at least kPersistentMinTiles tiles
+// and its LDS fits) runs one workgroup per CU that walks a list of units of
+// one XCD with the same tile loop; it loads K/V tiles straight from global
+// memory into LDS (row-major, XOR-swizzled rows) and reads V^T with the
+// transposing LDS read.  While a unit runs, the next unit's first three K/V
+// tiles are loaded into free tile buffers and its Q rows into a per-wave LDS
+// staging area, so the next unit starts from LDS instead of paying a burst
+// of HBM loads, and the finished unit's output stores drain while the next
+// one computes.
 //
 // The cyclic shift and the window gather are address arithmetic: a table of
 // the window's raster offsets is built in LDS per unit and every Q/K/V/O row
