@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "hilbert", "calib",
-                                       "all"),
+                                       "video", "all"),
                     default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
                          "at the same shape; 'copy': a plain device copy of known size, the "
@@ -430,6 +430,62 @@ def measure_backward(S, wl, sets, steps, stream):
                     "(pooled memory gradient folded in), dQ"}
 
 
+def measure_other_shape(S, wl, stream, dev, steps, dense_reps):
+    """Window attention (pool included, the workload's shift schedule) and the
+    in-build dense kernel at another of the pages' shapes.  Inputs are N(0,1)
+    drawn on the GPU (timing only; the seeded workload values are the parity
+    tests' business)."""
+    import torch
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    m, G = wl.window_tokens, wl.mem_tokens
+    g = torch.Generator(device=dev)
+    g.manual_seed(5000 + wl.seed)
+    q, k, v = (torch.randn((B, H, n, D), generator=g, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty_like(q)
+    mem = tuple(torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    pool, attn = [], []
+    for i in range(steps + 3):
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        S.pool_kv(k, v, wl.grid, wl.pool, out=mem)
+        ev[1].record(stream)
+        S.window_attn(q, k, v, wl.grid, wl.window, shift, mem=mem, out=out)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            pool.append(ev[0].elapsed_time(ev[1]))
+            attn.append(ev[1].elapsed_time(ev[2]))
+    a0 = []
+    for i in range(max(3, steps // 2) + 2):
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        S.window_attn(q, k, v, wl.grid, wl.window, shift, out=out)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            a0.append(ev[0].elapsed_time(ev[1]))
+    dense_ms = median(time_dense(S, [(q, k, v)], dense_reps, stream))
+    p_ms, a_ms, a0_ms = (sum(x) / len(x) for x in (pool, attn, a0))
+    fl = window_flops(B, H, n, m, G, D)
+    r = {"workload": wl.name, "n": n, "m": m, "G": G, "pool_kv_ms": p_ms, "window_attn_ms": a_ms,
+         "window_attn_tflops": fl / (a_ms * 1e-3) / 1e12,
+         "window_attn_mfma_frac": fl / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+         "window_attn_nomem_ms": a0_ms, "dense_ms": dense_ms,
+         "dense_tflops": dense_flops(B, H, n, D) / (dense_ms * 1e-3) / 1e12,
+         "speedup": {"theoretical_n_over_m": n / m, "realised_nomem": dense_ms / a0_ms,
+                     "realised_over_theoretical_nomem": dense_ms / a0_ms / (n / m),
+                     "theoretical_n_over_m_plus_G": n / (m + G), "realised_mem": dense_ms / a_ms,
+                     "realised_over_theoretical_mem": dense_ms / a_ms / (n / (m + G)),
+                     "realised_mem_incl_pool": dense_ms / (a_ms + p_ms)},
+         "data": "synthetic N(0,1) on the GPU"}
+    del q, k, v, out, mem
+    torch.cuda.empty_cache()
+    return r
+
+
 HILBERT_SIDES = (64, 128)    # token grids of 1024 x 1024 and 2048 x 2048 px images
 HILBERT_TILE = 256
 HILBERT_REGION = (8, 8)
@@ -576,6 +632,11 @@ def main():
         sets = make_sets(head, 2, dev)
         print(json.dumps(measure_backward(S, head, sets, args.steps, stream)))
         return
+    if args.only == "video":
+        print(json.dumps({"wan": measure_other_shape(S, W.WAN, stream, dev, args.steps, 3),
+                          "ultra": measure_other_shape(S, W.ULTRA, stream, dev,
+                                                       max(4, args.steps // 4), 2)}))
+        return
     if args.only == "calib":
         print(json.dumps(measure_mfma_peak(S, stream)))
         return
@@ -610,6 +671,13 @@ def main():
     print("[bench] hilbert tiles: " + ", ".join(
         f"{k} {v['tile_attn_ms']*1e3:.1f} us ({v['speedup_vs_dense']:.2f}x vs dense)"
         for k, v in hil.items() if k != "note"), file=sys.stderr, flush=True)
+    wan = measure_other_shape(S, W.WAN, stream, dev, max(8, args.steps // 4), 3)
+    wan["pages_context"] = ("up to 4.52x attention speedup on Wan (the pages' own dense baseline "
+                            "and hardware, not stated)")
+    ultra = measure_other_shape(S, W.ULTRA, stream, dev, 4, 2)
+    print(f"[bench] wan: attn {wan['window_attn_ms']*1e3:.0f} us ({wan['window_attn_tflops']:.0f} "
+          f"TFLOP/s), dense {wan['dense_ms']:.2f} ms; ultra: attn {ultra['window_attn_ms']:.2f} ms, "
+          f"dense {ultra['dense_ms']:.0f} ms", file=sys.stderr, flush=True)
     res_o = measure_window(S, other, args, stream, dev)
     print(f"[bench] {other.name}: attn {res_o['window_attn_ms']['mean']*1e3:.1f} us "
           f"({res_o['window_attn_tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
@@ -664,6 +732,7 @@ def main():
         "backward": bwd,
         "hilbert_tiles": hil,
         "mfma_calibration": calib,
+        "other_shapes": {"wan": wan, "ultra": ultra},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
