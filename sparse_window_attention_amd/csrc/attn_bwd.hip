@@ -145,10 +145,14 @@ __global__ void __launch_bounds__(256) bwd_dvec_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dq
+// Two 32-key tiles are staged per barrier and processed back to back.
+constexpr int kSubK = 2;
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   using T = BT<D>;
-  constexpr int kBuf = 2 * T::kRow + T::kTr;   // K rows, V rows, K^T
+  constexpr int kTile = 2 * T::kRow + T::kTr;   // K rows, V rows, K^T of 32 keys
+  constexpr int kBuf = kSubK * kTile;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nQT = (p.m + kUnit - 1) / kUnit;
   const int unit = xcd_unit(p.batch_heads * p.nW * nQT);
@@ -187,76 +191,87 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
 
   const int L = p.m + p.G;
-  const int nkt = (L + kBlk - 1) / kBlk;
+  constexpr int kIter = kSubK * kBlk;           // keys per iteration
+  const int nit = (L + kIter - 1) / kIter;
   const int lr = tid / T::CPR, lc = tid % T::CPR;
   const bool loader = lr < kBlk;
   const uint16_t* kmem = p.kmem + (int64_t)bh * p.G * D;
   const uint16_t* vmem = p.vmem + (int64_t)bh * p.G * D;
-  u32x4 kx{}, vx{};
-  auto load_tile = [&](int tile) __attribute__((always_inline)) {
-    const int key = min(tile * kBlk + lr, L - 1);
-    if (key < p.m) {
-      const uint32_t off = (uint32_t)tab[key] * stb + lc * 16;
-      kx = buf_load16(make_rsrc(p.k + base), off, 0);
-      vx = buf_load16(make_rsrc(p.v + base), off, 0);
-    } else {
-      const uint32_t off = (uint32_t)(key - p.m) * (D * 2) + lc * 16;
-      kx = buf_load16(make_rsrc(kmem), off, 0);
-      vx = buf_load16(make_rsrc(vmem), off, 0);
+  u32x4 kx[kSubK], vx[kSubK];
+  auto load_tiles = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < kSubK; ++sb) {
+      const int key = min(it * kIter + sb * kBlk + lr, L - 1);
+      if (key < p.m) {
+        const uint32_t off = (uint32_t)tab[key] * stb + lc * 16;
+        kx[sb] = buf_load16(make_rsrc(p.k + base), off, 0);
+        vx[sb] = buf_load16(make_rsrc(p.v + base), off, 0);
+      } else {
+        const uint32_t off = (uint32_t)(key - p.m) * (D * 2) + lc * 16;
+        kx[sb] = buf_load16(make_rsrc(kmem), off, 0);
+        vx[sb] = buf_load16(make_rsrc(vmem), off, 0);
+      }
     }
   };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* sk = reinterpret_cast<uint16_t*>(smem + buf * kBuf);
-    uint16_t* sv = sk + kBlk * T::KS;
-    uint16_t* st = sv + kBlk * T::KS;
-    *reinterpret_cast<u32x4*>(sk + lr * T::KS + lc * 8) = kx;
-    *reinterpret_cast<u32x4*>(sv + lr * T::KS + lc * 8) = vx;
-    store_tr<T::TS>(st, lr, lc * 8, kx);
+  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < kSubK; ++sb) {
+      uint16_t* sk = reinterpret_cast<uint16_t*>(smem + buf * kBuf + sb * kTile);
+      uint16_t* sv = sk + kBlk * T::KS;
+      uint16_t* st = sv + kBlk * T::KS;
+      *reinterpret_cast<u32x4*>(sk + lr * T::KS + lc * 8) = kx[sb];
+      *reinterpret_cast<u32x4*>(sv + lr * T::KS + lc * 8) = vx[sb];
+      store_tr<T::TS>(st, lr, lc * 8, kx[sb]);
+    }
   };
   if (loader) {
-    load_tile(0);
-    store_tile(0);
+    load_tiles(0);
+    store_tiles(0);
   }
   __syncthreads();
   const float c1 = p.c1;
-  for (int t = 0; t < nkt; ++t) {
-    if (loader && t + 1 < nkt) load_tile(t + 1);
-    const uint16_t* sk = reinterpret_cast<const uint16_t*>(smem + (t & 1) * kBuf);
-    const uint16_t* sv = sk + kBlk * T::KS;
-    const uint16_t* st = sv + kBlk * T::KS;
-    f32x16 s{}, dp{};
+  for (int it = 0; it < nit; ++it) {
+    if (loader && it + 1 < nit) load_tiles(it + 1);
 #pragma unroll
-    for (int ss = 0; ss < T::QS; ++ss) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sk + l32 * T::KS + hf * (D / 2) + ss * 8);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(sv + l32 * T::KS + hf * (D / 2) + ss * 8);
-      s = mfma(a, qreg[ss], s);
-      dp = mfma(b, dreg[ss], dp);
-    }
-    u32x4 dsb[2];
+    for (int sb = 0; sb < kSubK; ++sb) {
+      const int t = it * kSubK + sb;              // 32-key tile index
+      const uint16_t* sk = reinterpret_cast<const uint16_t*>(smem + (it & 1) * kBuf + sb * kTile);
+      const uint16_t* sv = sk + kBlk * T::KS;
+      const uint16_t* st = sv + kBlk * T::KS;
+      f32x16 s{}, dp{};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * u + j;
-        const int key = t * kBlk + acc_row(r, hf);
-        float x = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
-        x = key < L ? x : -INFINITY;
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lse2));
-        e[j] = pr * (dp[r] - dval);
+      for (int ss = 0; ss < T::QS; ++ss) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + l32 * T::KS + hf * (D / 2) + ss * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(sv + l32 * T::KS + hf * (D / 2) + ss * 8);
+        s = mfma(a, qreg[ss], s);
+        dp = mfma(b, dreg[ss], dp);
       }
-      dsb[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                     pack_bf16x2(e[6], e[7])};
-    }
+      u32x4 dsb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        float e[8];
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(st + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-        acc[db] = mfma(a, dsb[u], acc[db]);
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * u + j;
+          const int key = t * kBlk + acc_row(r, hf);
+          float x = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
+          x = key < L ? x : -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lse2));
+          e[j] = pr * (dp[r] - dval);
+        }
+        dsb[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                       pack_bf16x2(e[6], e[7])};
       }
-    if (loader && t + 1 < nkt) store_tile((t + 1) & 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(st + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
+          acc[db] = mfma(a, dsb[u], acc[db]);
+        }
+    }
+    if (loader && it + 1 < nit) store_tiles((it + 1) & 1);
     __syncthreads();
   }
   store_rows<D>(acc, p.scale, nullptr, p.dq + base, qoff, qvalid, hf);
@@ -551,7 +566,7 @@ int launch_d(const BwdParams& p, hipStream_t stream) {
   if ((rc = launch_dkdv<D, false, 0>(p, stream))) return rc;
   if ((rc = launch_dkdv<D, false, 1>(p, stream))) return rc;
   {
-    constexpr int kBuf = 2 * T::kRow + T::kTr;
+    constexpr int kBuf = kSubK * (2 * T::kRow + T::kTr);
     const size_t lds = 2 * kBuf + (size_t)p.m * 4;
     if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
     const int64_t units = (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
