@@ -20,10 +20,11 @@
 //            S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
 //   dkdv     key-stationary: 256 keys (32 per wave) against blocks of 32
 //            queries: S = Q K^T, P; pass 0: dV^T += dO^T P; pass 1:
-//            dP = dO V^T, dS, dK^T += Q^T dS.  Memory-key units cover one
-//            chunk of the head's queries each and write fp32 partial sums;
-//            window-key units write the final dK, dV of their tokens, adding
-//            the pooled memory gradient of the token's cell.
+//            dP = dO V^T, dS, dK^T += Q^T dS.  Both passes run in one grid
+//            (one launch for memory keys, one for window keys).  Memory-key
+//            units cover one chunk of the head's queries each and write fp32
+//            partial sums; window-key units write the final dK, dV of their
+//            tokens, adding the pooled memory gradient of the token's cell.
 //   memsum   sums the memory partials and divides by the cell size
 // All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 as operands.  Transposed LDS tiles order their k index the
@@ -56,11 +57,13 @@ __device__ __forceinline__ int64_t slice_base(const BwdParams& p, int bh) {
   return (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
 }
 
-// Unit of this workgroup with consecutive units on one XCD; -1 past the end.
-__device__ __forceinline__ int xcd_unit(int units) {
+// Unit of workgroup `blk` with consecutive units on one XCD; -1 past the
+// end.  Workgroups are dealt to the XCDs round robin, so blk & 7 is the XCD
+// as long as blk differs from the block index by a multiple of 8.
+__device__ __forceinline__ int xcd_unit(int units, int blk) {
   const int upx = (units + 7) / 8;
-  const int slot = blockIdx.x >> 3;
-  const int u = (blockIdx.x & 7) * upx + slot;
+  const int slot = blk >> 3;
+  const int u = (blk & 7) * upx + slot;
   return (slot < upx && u < units) ? u : -1;
 }
 
@@ -155,7 +158,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   constexpr int kBuf = kSubK * kTile;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nQT = (p.m + kUnit - 1) / kUnit;
-  const int unit = xcd_unit(p.batch_heads * p.nW * nQT);
+  const int unit = xcd_unit(p.batch_heads * p.nW * nQT, blockIdx.x);
   if (unit < 0) return;
   const int qt = unit % nQT;
   const int rest = unit / nQT;
@@ -297,7 +300,7 @@ struct DkdvLayout {
 };
 
 template <int D, bool MEM, int PASS>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   using T = BT<D>;
   using DL = DkdvLayout<D, PASS>;
   constexpr int kMain = DL::kMain;
@@ -306,7 +309,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   int bh, kbase, nq, qbase = 0, win = 0;
   if constexpr (MEM) {
     const int nmc = (p.G + kUnit - 1) / kUnit;
-    const int unit = xcd_unit(p.batch_heads * nmc * p.nqc);
+    const int unit = xcd_unit(p.batch_heads * nmc * p.nqc, blk);
     if (unit < 0) return;
     const int qc = unit % p.nqc;
     const int rest = unit / p.nqc;
@@ -316,7 +319,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
     nq = min(p.qchunk, p.n - qbase);
   } else {
     const int nkc = (p.m + kUnit - 1) / kUnit;
-    const int unit = xcd_unit(p.batch_heads * p.nW * nkc);
+    const int unit = xcd_unit(p.batch_heads * p.nW * nkc, blk);
     if (unit < 0) return;
     kbase = (unit % nkc) * kUnit;
     const int rest = unit / nkc;
@@ -504,6 +507,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// Both passes in one grid: workgroups [0, split) run pass 0 (dV), the rest
+// pass 1 (dK); split is a multiple of 8.  One launch lets the second pass
+// fill the CUs the first leaves idle at its end.
+template <int D, bool MEM>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p, int split) {
+  if ((int)blockIdx.x < split) dkdv_body<D, MEM, 0>(p, blockIdx.x);
+  else dkdv_body<D, MEM, 1>(p, blockIdx.x - split);
+}
+
 // ---------------------------------------------------------------- memsum
 template <int D>
 __global__ void __launch_bounds__(256) bwd_memsum_kernel(BwdParams p, float inv_cell) {
@@ -530,17 +542,18 @@ int set_lds(K kernel, size_t bytes) {
              : BASA_ERR_HIP;
 }
 
-template <int D, bool MEM, int PASS>
+template <int D, bool MEM>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
-  const size_t lds = 2 * (size_t)DkdvLayout<D, PASS>::kBuf + (MEM ? 0 : (size_t)p.m * 4);
+  const size_t lds = 2 * (size_t)max(DkdvLayout<D, 0>::kBuf, DkdvLayout<D, 1>::kBuf) +
+                     (MEM ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
   const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + kUnit - 1) / kUnit) * p.nqc
                             : (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
-  if (units > INT32_MAX / 2) return BASA_ERR_UNSUPPORTED;
-  if (set_lds(&bwd_dkdv_kernel<D, MEM, PASS>, lds)) return BASA_ERR_HIP;
-  const int64_t upx = (units + 7) / 8;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MEM, PASS>), dim3((unsigned)(8 * upx)), dim3(kThreads),
-                     lds, stream, p);
+  if (units > INT32_MAX / 4) return BASA_ERR_UNSUPPORTED;
+  if (set_lds(&bwd_dkdv_kernel<D, MEM>, lds)) return BASA_ERR_HIP;
+  const int64_t per_pass = 8 * ((units + 7) / 8);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MEM>), dim3((unsigned)(2 * per_pass)), dim3(kThreads), lds,
+                     stream, p, (int)per_pass);
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
@@ -556,15 +569,13 @@ int launch_d(const BwdParams& p, hipStream_t stream) {
   }
   int rc;
   if (p.G > 0) {
-    if ((rc = launch_dkdv<D, true, 0>(p, stream))) return rc;
-    if ((rc = launch_dkdv<D, true, 1>(p, stream))) return rc;
+    if ((rc = launch_dkdv<D, true>(p, stream))) return rc;
     const int64_t total = (int64_t)p.batch_heads * p.G * D;
     hipLaunchKernelGGL((bwd_memsum_kernel<D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, p, 1.0f / (float)(p.pt * p.py * p.px));
     if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
   }
-  if ((rc = launch_dkdv<D, false, 0>(p, stream))) return rc;
-  if ((rc = launch_dkdv<D, false, 1>(p, stream))) return rc;
+  if ((rc = launch_dkdv<D, false>(p, stream))) return rc;
   {
     constexpr int kBuf = kSubK * (2 * T::kRow + T::kTr);
     const size_t lds = 2 * kBuf + (size_t)p.m * 4;
