@@ -286,35 +286,71 @@ struct Core {
   __device__ static __forceinline__ int swz_k(int r) { return (r / RPB) & (TL::CPR - 1); }
   __device__ static __forceinline__ int swz_v(int r) { return (4 * (r / RPB)) & (TL::CPR - 4); }
 
-  // Issues this wave's share of the loads of tile `tile` (K or V) into `buf`.
-  __device__ __forceinline__ void dma_tile(unsigned char* buf, const Unit& u, const uint32_t* t,
-                                           int tile, bool isv) const {
+  // Issues this wave's share of the loads of a V tile and a K tile (either
+  // may be skipped) into their buffers.  The tile kind is decided once per
+  // tile, and the window-offset table reads of both tiles go out before any
+  // load, so one wait on LDS covers them.
+  __device__ __forceinline__ void dma_pair(bool dv, unsigned char* bv, const Unit& uv,
+                                           const uint32_t* tv, int tilev, bool dk,
+                                           unsigned char* bk, const Unit& uk, const uint32_t* tk,
+                                           int tilek) const {
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int k0 = tile * kKT;
+    int r[kDmaIpw];
+#pragma unroll
+    for (int i = 0; i < kDmaIpw; ++i) r[i] = ((wv * kDmaIpw + i) * 64 + lane) / TL::CPR;
+    const int kv0 = tilev * kKT, kk0 = tilek * kKT;
+    const bool winv = !FULL && kv0 + kKT <= m, wink = !FULL && kk0 + kKT <= m;
+    uint32_t ov[kDmaIpw], ok[kDmaIpw];
 #pragma unroll
     for (int i = 0; i < kDmaIpw; ++i) {
-      const int ins = wv * kDmaIpw + i;
-      const int r = (ins * 64 + lane) / TL::CPR;
-      const uint32_t cb = (uint32_t)(((lane % TL::CPR) ^ (isv ? swz_v(r) : swz_k(r))) * 16);
-      auto* lds = (__attribute__((address_space(3))) void*)(buf + ins * 1024);
-      if constexpr (FULL) {
-        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, (uint32_t)min(k0 + r, L - 1) * stb + cb,
-                                                 0, 0, 0);
-      } else if (k0 + kKT <= m) {
-        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, t[k0 + r] + cb, 0, 0, 0);
-      } else if (k0 >= m && k0 + kKT <= L) {
-        const Rsrc rs = make_rsrc((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, (uint32_t)r * (D * 2) + cb,
-                                                 (uint32_t)(k0 - m) * (D * 2), 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(row_ptr(u, t, k0 + r, isv) + cb), lds,
-            16, 0, 0);
-      }
+      ov[i] = (dv && winv) ? tv[kv0 + r[i]] : 0u;
+      ok[i] = (dk && wink) ? tk[kk0 + r[i]] : 0u;
     }
+    if (dv) dma_issue(bv, uv, tv, kv0, true, r, ov);
+    if (dk) dma_issue(bk, uk, tk, kk0, false, r, ok);
+  }
+  __device__ __forceinline__ void dma_issue(unsigned char* buf, const Unit& u, const uint32_t* t,
+                                            int k0, bool isv, const int (&r)[kDmaIpw],
+                                            const uint32_t (&off)[kDmaIpw]) const {
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t cb[kDmaIpw];
+#pragma unroll
+    for (int i = 0; i < kDmaIpw; ++i)
+      cb[i] = (uint32_t)(((lane % TL::CPR) ^ (isv ? swz_v(r[i]) : swz_k(r[i]))) * 16);
+    auto lds = [&](int i) __attribute__((always_inline)) {
+      return (__attribute__((address_space(3))) void*)(buf + (wv * kDmaIpw + i) * 1024);
+    };
+    if constexpr (FULL) {
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+#pragma unroll
+      for (int i = 0; i < kDmaIpw; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16,
+                                                 (uint32_t)min(k0 + r[i], L - 1) * stb + cb[i], 0, 0, 0);
+    } else if (k0 + kKT <= m) {
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+#pragma unroll
+      for (int i = 0; i < kDmaIpw; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16, off[i] + cb[i], 0, 0, 0);
+    } else if (k0 >= m && k0 + kKT <= L) {
+      const Rsrc rs = make_rsrc((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
+#pragma unroll
+      for (int i = 0; i < kDmaIpw; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16, (uint32_t)r[i] * (D * 2) + cb[i],
+                                                 (uint32_t)(k0 - m) * (D * 2), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDmaIpw; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(row_ptr(u, t, k0 + r[i], isv) + cb[i]),
+            lds(i), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void dma_tile(unsigned char* buf, const Unit& u, const uint32_t* t,
+                                           int tile, bool isv) const {
+    if (isv) dma_pair(true, buf, u, t, tile, false, buf, u, t, 0);
+    else dma_pair(false, buf, u, t, 0, true, buf, u, t, tile);
   }
   // S^T = K Q^T with K from a swizzled tile.  Row kb*32 + l32 has the
   // swizzle x of row l32 (32 rows span whole swizzle periods); chunk
@@ -835,10 +871,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     // loads into LDS go out only after this barrier: until then other waves
     // may still read the buffers (the previous unit's last V tile).
     lds_barrier();
-    if constexpr (DMA) {
-      get_v(uc, tab, 1);
-      get_k(uc, tab, 2);
-    }
+    if constexpr (DMA) c.dma_pair(true, dV(1), uc, tab, 1, true, dK(0), uc, tab, 2);
     if (!FULL && j >= 1 && has_next) c.build_table(tab_of(j + 1), un.win);
 
     // Iteration t: as in the unit kernel; the loads past the unit's last tile
@@ -860,15 +893,27 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       }
       lds_barrier();
       const int tv = t + 2, tk = t + 3;
-      if (tv < nkt || (has_next && tv == nkt)) {
-        const bool cur = tv < nkt;
-        const Unit u = cur ? uc : un;  // by value: the choice stays in registers
-        get_v(u, cur ? tab : tabn, cur ? tv : 0);
-      }
-      if (tk < nkt || (has_next && tk <= nkt + 1)) {
-        const bool cur = tk < nkt;
-        const Unit u = cur ? uc : un;
-        get_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
+      const bool do_v = tv < nkt || (has_next && tv == nkt);
+      const bool do_k = tk < nkt || (has_next && tk <= nkt + 1);
+      if constexpr (DMA) {
+        const bool cv = tv < nkt, ck = tk < nkt;
+        const int jv = cv ? tv : 0, jk = ck ? tk : tk - nkt;
+        const Unit u_v = cv ? uc : un;  // by value: the choice stays in registers
+        const Unit u_k = ck ? uc : un;
+        if (do_v || do_k)
+          c.dma_pair(do_v, dV(jv & 1), u_v, cv ? tab : tabn, jv, do_k, dK(jk & 1), u_k,
+                     ck ? tab : tabn, jk);
+      } else {
+        if (do_v) {
+          const bool cur = tv < nkt;
+          const Unit u = cur ? uc : un;  // by value: the choice stays in registers
+          get_v(u, cur ? tab : tabn, cur ? tv : 0);
+        }
+        if (do_k) {
+          const bool cur = tk < nkt;
+          const Unit u = cur ? uc : un;
+          get_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
+        }
       }
       if (has_next && t < qstep)
         if constexpr (BASA_PERSISTENT_QSTAGE) {
