@@ -361,16 +361,25 @@ struct Core {
     constexpr int H = TL::CPR / 2;
     const int x = swz_k(l32);
     const uint32_t kbase = (uint32_t)(l32 * (TL::CPR * 16) + 16 * ((hf * H) ^ (x & H)) + 16 * (x & (H - 1)));
+    // operands of step ss+1 are read before the products of step ss
+    u32x4 a[2][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      a[0][kb] = *reinterpret_cast<const u32x4*>(kt + kbase + kb * 32 * (TL::CPR * 16));
 #pragma unroll
     for (int ss = 0; ss < QS; ++ss) {
-      const uint32_t off = kbase ^ (uint32_t)(16 * ss);
+      if (ss + 1 < QS) {
+        const uint32_t off = kbase ^ (uint32_t)(16 * (ss + 1));
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          a[(ss + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(kt + off + kb * 32 * (TL::CPR * 16));
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + off + kb * 32 * (TL::CPR * 16));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qreg[qb][ss]),
+              __builtin_bit_cast(bf16x8, a[ss & 1][kb]), __builtin_bit_cast(bf16x8, qreg[qb][ss]),
               ss == 0 ? zero16 : s[qb][kb], 0, 0, 0);
       }
     }
@@ -388,23 +397,28 @@ struct Core {
     const int sq = (lane & 15) >> 2;       // row within the 4-row group
     const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
     const uint32_t lanev = (uint32_t)((4 * hf + sq) * (TL::CPR * 16) + (d0 & 7) * 2);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    // operands of product i+1 are read before product i
+    constexpr int NP = DB * 2 * KB;
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int db = i / (2 * KB), sl = i % (2 * KB);
       const uint32_t vb = lanev + (uint32_t)((((4 * db + (d0 >> 3)) ^ swz_v(sq)) * 16));
+      bf16x4 h2[2];
 #pragma unroll
-      for (int sl = 0; sl < 2 * KB; ++sl) {
-        bf16x4 h2[2];
+      for (int h = 0; h < 2; ++h)
+        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
+            vt + vb + (16 * sl + 8 * h) * (TL::CPR * 16)));
+      return bf16x8{h2[0][0], h2[0][1], h2[0][2], h2[0][3], h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+    };
+    bf16x8 av[2];
+    av[0] = rd(0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
-              vt + vb + (16 * sl + 8 * h) * (TL::CPR * 16)));
-        const bf16x8 av = {h2[0][0], h2[0][1], h2[0][2], h2[0][3],
-                           h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+    for (int i = 0; i < NP; ++i) {
+      if (i + 1 < NP) av[(i + 1) & 1] = rd(i + 1);
+      const int db = i / (2 * KB), sl = i % (2 * KB);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              av, __builtin_bit_cast(bf16x8, pb[qb][sl]), acc[qb][db], 0, 0, 0);
-      }
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            av[i & 1], __builtin_bit_cast(bf16x8, pb[qb][sl]), acc[qb][db], 0, 0, 0);
     }
   }
 
