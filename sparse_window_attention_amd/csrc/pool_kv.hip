@@ -9,11 +9,12 @@
 //
 // A streaming reduction bound by HBM bandwidth.  One wave per (batch, head,
 // cell): the CPR lanes of a lane group hold the 16-byte chunks of one token
-// row (so every load instruction reads whole rows), and the 64 / CPR lane
-// groups split the cell's pt*py grid rows between them.  Each lane walks the
-// px tokens of its rows for K and V, then the groups' partial sums are added
-// with lane exchanges.  fp32 accumulation; bf16 results rounded to nearest
-// even.
+// row, and the 64 / CPR lane groups take interleaved tokens of each grid row
+// of the cell, so every load instruction reads consecutive tokens.  Rows and
+// frames are walked by pointer steps, with no integer division per token.
+// Each lane accumulates its tokens of K and V, then the groups' partial sums
+// are added with lane exchanges.  fp32 accumulation; bf16 results rounded to
+// nearest even.
 #include "basa_common.h"
 #include "basa_internal.h"
 
@@ -62,29 +63,33 @@ __global__ void __launch_bounds__(kWavesPerBlock * 64) pool_kernel(PoolParams p,
   float ks[8], vs[8];  // the first NA are live
 #pragma unroll
   for (int e = 0; e < 8; ++e) ks[e] = vs[e] = 0.0f;
-  const int rows = p.pt * p.py;       // grid rows of the cell, split over lane groups
-  for (int rr = grp; rr < rows; rr += NG) {
-    const int a = rr / p.py, c = rr - a * p.py;
-    const int64_t row = ((int64_t)(gt * p.pt + a) * p.Hg + (gy * p.py + c)) * p.Wg + gx * p.px;
-    const char* kr = kb + row * tokb;
-    const char* vr = vb + row * tokb;
-    int x = 0;
-    for (; x + 4 <= p.px; x += 4) {
-      u32x4 kk[4], vv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        kk[u] = *reinterpret_cast<const u32x4*>(kr + (x + u) * tokb);
-        vv[u] = *reinterpret_cast<const u32x4*>(vr + (x + u) * tokb);
+  // Lane group grp takes the tokens x = grp, grp + NG, ... of every grid row
+  // of the cell, so one load instruction reads NG consecutive tokens of one
+  // row.  Rows and frames advance by pointer steps: no division per token.
+  const int64_t rowstep = (int64_t)p.Wg * tokb;           // next grid row
+  const int64_t framestep = (int64_t)p.Hg * p.Wg * tokb;  // next frame
+  const int64_t cell0 = ((int64_t)(gt * p.pt) * p.Hg + gy * p.py) * p.Wg + gx * p.px;
+  const char* kf = kb + cell0 * tokb;
+  const char* vf = vb + cell0 * tokb;
+  for (int a = 0; a < p.pt; ++a, kf += framestep, vf += framestep) {
+    const char* kr = kf;
+    const char* vr = vf;
+    for (int c = 0; c < p.py; ++c, kr += rowstep, vr += rowstep) {
+      int x = grp;
+      for (; x + NG < p.px; x += 2 * NG) {
+        const u32x4 k0 = *reinterpret_cast<const u32x4*>(kr + x * tokb);
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vr + x * tokb);
+        const u32x4 k1 = *reinterpret_cast<const u32x4*>(kr + (x + NG) * tokb);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vr + (x + NG) * tokb);
+        accumulate<BF16>(ks, k0);
+        accumulate<BF16>(vs, v0);
+        accumulate<BF16>(ks, k1);
+        accumulate<BF16>(vs, v1);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        accumulate<BF16>(ks, kk[u]);
-        accumulate<BF16>(vs, vv[u]);
+      if (x < p.px) {
+        accumulate<BF16>(ks, *reinterpret_cast<const u32x4*>(kr + x * tokb));
+        accumulate<BF16>(vs, *reinterpret_cast<const u32x4*>(vr + x * tokb));
       }
-    }
-    for (; x < p.px; ++x) {
-      accumulate<BF16>(ks, *reinterpret_cast<const u32x4*>(kr + x * tokb));
-      accumulate<BF16>(vs, *reinterpret_cast<const u32x4*>(vr + x * tokb));
     }
   }
   // add the lane groups' partial sums: groups differ in the lane bits above CPR
