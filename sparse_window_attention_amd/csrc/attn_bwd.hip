@@ -16,8 +16,9 @@
 // Kernels (one workgroup of 8 waves per unit, XCD-aware unit order):
 //   dvec     Dv for every token
 //   dq       query-stationary: 256 queries of a window against the key
-//            sequence [window keys; memory keys] in tiles of 32 keys:
-//            S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//            sequence [window keys; memory keys] in tiles of 64 keys loaded
+//            straight into LDS: S^T = K Q^T, dP^T = V dO^T, dS^T,
+//            dQ^T += K^T dS^T (K^T by transposing LDS reads)
 //   dkdv     key-stationary: 256 keys (32 per wave) against blocks of 32
 //            queries: S = Q K^T, P; pass 0: dV^T += dO^T P; pass 1:
 //            dP = dO V^T, dS, dK^T += Q^T dS.  Both passes run in one grid
@@ -35,6 +36,7 @@
 namespace basa {
 
 namespace {
+
 
 constexpr int kNW = 8;                 // waves per workgroup
 constexpr int kThreads = kNW * 64;
@@ -148,15 +150,35 @@ __global__ void __launch_bounds__(256) bwd_dvec_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dq
-// Two 32-key tiles are staged per barrier and processed back to back.
-constexpr int kSubK = 2;
+// dQ with the key tiles loaded straight into LDS: 64 keys per iteration, K
+// and V tiles row-major (16-byte chunks XOR-swizzled per row), K rows and V
+// rows read as MFMA operands and K^T read with the transposing LDS read.  One
+// swizzle serves both reads of the K tile: chunk c of row r sits at slot
+// c ^ f(r), f a bijection of r mod 16 whose bits 2-3 separate any 4
+// consecutive rows, so the 16 rows of a quarter-wave row read and the
+// 4 rows x 4 chunks of a half-wave transposing read fall in distinct banks.
+template <int D>
+struct DqDma {
+  using T = BT<D>;
+  static constexpr int kKeys = 64;                  // keys per iteration
+  static constexpr int CPR = D / 8;
+  static constexpr int RowB = CPR * 16;             // bytes per row
+  static constexpr int kTileB = kKeys * RowB;       // one K or V tile
+  static constexpr int kIpw = kTileB / 1024 / kNW;  // 1 KB loads per wave and tile
+  static_assert(kIpw >= 1 && kIpw * kNW * 1024 == kTileB, "tile must split over the waves");
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+};
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   using T = BT<D>;
-  constexpr int kTile = 2 * T::kRow + T::kTr;   // K rows, V rows, K^T of 32 keys
-  constexpr int kBuf = kSubK * kTile;
+  using Q = DqDma<D>;
+  constexpr int CPR = Q::CPR, RowB = Q::RowB, KTB = Q::kTileB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // K buffer b at b * KTB, V buffer b at (2 + b) * KTB, then the table
   const int nQT = (p.m + kUnit - 1) / kUnit;
   const int unit = xcd_unit(p.batch_heads * p.nW * nQT, blockIdx.x);
   if (unit < 0) return;
@@ -167,11 +189,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   const int64_t base = slice_base(p, bh);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
   const uint32_t stb = (uint32_t)p.stride_tok * 2u;
-  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBuf);
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + 4 * KTB);
   for (int r = tid; r < p.m; r += kThreads) tab[r] = window_token(p.geo, win, r);
   __syncthreads();
 
-  // this lane's query: Q and dO rows as B operands, its lse and Dv
   const int qr = qt * kUnit + wave * 32 + l32;
   const bool qvalid = qr < p.m;
   const int qtok = qvalid ? tab[qr] : 0;
@@ -194,58 +215,67 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
 
   const int L = p.m + p.G;
-  constexpr int kIter = kSubK * kBlk;           // keys per iteration
-  const int nit = (L + kIter - 1) / kIter;
-  const int lr = tid / T::CPR, lc = tid % T::CPR;
-  const bool loader = lr < kBlk;
+  const int nit = (L + Q::kKeys - 1) / Q::kKeys;
   const uint16_t* kmem = p.kmem + (int64_t)bh * p.G * D;
   const uint16_t* vmem = p.vmem + (int64_t)bh * p.G * D;
-  u32x4 kx[kSubK], vx[kSubK];
-  auto load_tiles = [&](int it) __attribute__((always_inline)) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // this wave's share of the loads of iteration it's K and V tiles
+  auto dma = [&](int it) __attribute__((always_inline)) {
+    const int k0 = it * Q::kKeys;
+    unsigned char* bk = smem + (it & 1) * KTB;
+    unsigned char* bv = smem + (2 + (it & 1)) * KTB;
 #pragma unroll
-    for (int sb = 0; sb < kSubK; ++sb) {
-      const int key = min(it * kIter + sb * kBlk + lr, L - 1);
-      if (key < p.m) {
-        const uint32_t off = (uint32_t)tab[key] * stb + lc * 16;
-        kx[sb] = buf_load16(make_rsrc(p.k + base), off, 0);
-        vx[sb] = buf_load16(make_rsrc(p.v + base), off, 0);
+    for (int i = 0; i < Q::kIpw; ++i) {
+      const int ins = wv * Q::kIpw + i;
+      const int r = (ins * 64 + lane) / CPR;
+      const uint32_t cb = (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
+      auto* lk = (__attribute__((address_space(3))) void*)(bk + ins * 1024);
+      auto* lv = (__attribute__((address_space(3))) void*)(bv + ins * 1024);
+      if (k0 + Q::kKeys <= p.m) {
+        const uint32_t off = (uint32_t)tab[k0 + r] * stb + cb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.k + base), lk, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.v + base), lv, 16, off, 0, 0, 0);
+      } else if (k0 >= p.m && k0 + Q::kKeys <= L) {
+        const uint32_t off = (uint32_t)(k0 - p.m + r) * (D * 2) + cb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kmem), lk, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vmem), lv, 16, off, 0, 0, 0);
       } else {
-        const uint32_t off = (uint32_t)(key - p.m) * (D * 2) + lc * 16;
-        kx[sb] = buf_load16(make_rsrc(kmem), off, 0);
-        vx[sb] = buf_load16(make_rsrc(vmem), off, 0);
+        const int key = min(k0 + r, L - 1);   // rows past the end: clamped, masked below
+        const char* gk;
+        const char* gvp;
+        if (key < p.m) {
+          const int64_t o = (int64_t)tab[key] * stb + cb;
+          gk = reinterpret_cast<const char*>(p.k + base) + o;
+          gvp = reinterpret_cast<const char*>(p.v + base) + o;
+        } else {
+          const int64_t o = (int64_t)(key - p.m) * (D * 2) + cb;
+          gk = reinterpret_cast<const char*>(kmem) + o;
+          gvp = reinterpret_cast<const char*>(vmem) + o;
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gk, lk, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gvp, lv, 16, 0, 0);
       }
     }
   };
-  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int sb = 0; sb < kSubK; ++sb) {
-      uint16_t* sk = reinterpret_cast<uint16_t*>(smem + buf * kBuf + sb * kTile);
-      uint16_t* sv = sk + kBlk * T::KS;
-      uint16_t* st = sv + kBlk * T::KS;
-      *reinterpret_cast<u32x4*>(sk + lr * T::KS + lc * 8) = kx[sb];
-      *reinterpret_cast<u32x4*>(sv + lr * T::KS + lc * 8) = vx[sb];
-      store_tr<T::TS>(st, lr, lc * 8, kx[sb]);
-    }
-  };
-  if (loader) {
-    load_tiles(0);
-    store_tiles(0);
-  }
+  dma(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads are in LDS
   __syncthreads();
   const float c1 = p.c1;
+  const int x = Q::swz(l32);
+  const int sq = (lane & 15) >> 2;
+  const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
   for (int it = 0; it < nit; ++it) {
-    if (loader && it + 1 < nit) load_tiles(it + 1);
+    if (it + 1 < nit) dma(it + 1);
+    const unsigned char* sk = smem + (it & 1) * KTB;
+    const unsigned char* sv = smem + (2 + (it & 1)) * KTB;
 #pragma unroll
-    for (int sb = 0; sb < kSubK; ++sb) {
-      const int t = it * kSubK + sb;              // 32-key tile index
-      const uint16_t* sk = reinterpret_cast<const uint16_t*>(smem + (it & 1) * kBuf + sb * kTile);
-      const uint16_t* sv = sk + kBlk * T::KS;
-      const uint16_t* st = sv + kBlk * T::KS;
+    for (int kb = 0; kb < 2; ++kb) {
       f32x16 s{}, dp{};
 #pragma unroll
       for (int ss = 0; ss < T::QS; ++ss) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + l32 * T::KS + hf * (D / 2) + ss * 8);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(sv + l32 * T::KS + hf * (D / 2) + ss * 8);
+        const int off = (kb * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + off);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(sv + off);
         s = mfma(a, qreg[ss], s);
         dp = mfma(b, dreg[ss], dp);
       }
@@ -256,25 +286,37 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * u + j;
-          const int key = t * kBlk + acc_row(r, hf);
-          float x = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
-          x = key < L ? x : -INFINITY;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lse2));
+          const int key = it * Q::kKeys + kb * 32 + acc_row(r, hf);
+          float xv = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
+          xv = key < L ? xv : -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(xv, c1, -lse2));
           e[j] = pr * (dp[r] - dval);
         }
         dsb[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                        pack_bf16x2(e[6], e[7])};
       }
+      // dQ^T += K^T dS^T: K^T of slice sl = 2kb + u by transposing reads
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        const int sl = 2 * kb + u;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(st + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-          acc[db] = mfma(a, dsb[u], acc[db]);
+          bf16x4 h2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int key = 16 * sl + 8 * h + 4 * hf + sq;
+            const int d = 32 * db + d0;
+            h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
+                sk + key * RowB + (((d >> 3) ^ Q::swz(key)) * 16) + (d & 7) * 2));
+          }
+          const bf16x8 av = {h2[0][0], h2[0][1], h2[0][2], h2[0][3],
+                             h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, dsb[u]),
+                                                           acc[db], 0, 0, 0);
         }
+      }
     }
-    if (loader && it + 1 < nit) store_tiles((it + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next tiles
     __syncthreads();
   }
   store_rows<D>(acc, p.scale, nullptr, p.dq + base, qoff, qvalid, hf);
@@ -577,14 +619,13 @@ int launch_d(const BwdParams& p, hipStream_t stream) {
   }
   if ((rc = launch_dkdv<D, false>(p, stream))) return rc;
   {
-    constexpr int kBuf = kSubK * (2 * T::kRow + T::kTr);
-    const size_t lds = 2 * kBuf + (size_t)p.m * 4;
-    if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
     const int64_t units = (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
-    if (set_lds(&bwd_dq_kernel<D>, lds)) return BASA_ERR_HIP;
     const int64_t upx = (units + 7) / 8;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(8 * upx)), dim3(kThreads), lds, stream,
-                       p);
+    const size_t lds = 4 * (size_t)DqDma<D>::kTileB + (size_t)p.m * 4;
+    if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
+    if (set_lds(&bwd_dq_kernel<D>, lds)) return BASA_ERR_HIP;
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(8 * upx)), dim3(kThreads), lds,
+                       stream, p);
     if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
   }
   return BASA_OK;
