@@ -28,8 +28,10 @@
 //            tokens, adding the pooled memory gradient of the token's cell.
 //   memsum   sums the memory partials and divides by the cell size
 // All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
-// rounded to bf16 as operands.  Transposed LDS tiles order their k index the
-// way the S accumulators hold it (vslot), as in the forward's V^T.
+// rounded to bf16 as operands.  Tiles are loaded straight into LDS row-major;
+// the transposed operands (K^T, dO^T, Q^T) are read with the transposing LDS
+// read, whose lane addresses give the k index the key (or query) order in
+// which the S accumulators hold P and dS.
 #include "basa_common.h"
 #include "basa_internal.h"
 
@@ -37,18 +39,13 @@ namespace basa {
 
 namespace {
 
-
 constexpr int kNW = 8;                 // waves per workgroup
 constexpr int kThreads = kNW * 64;
-constexpr int kBlk = 32;               // keys per dq tile, queries per dkdv block
+constexpr int kBlk = 32;               // rows of one MFMA block: keys (dq), queries (dkdv)
 constexpr int kUnit = kNW * 32;        // queries per dq unit, keys per dkdv unit
 
 template <int D>
 struct BT {
-  static constexpr int KS = D + 8;              // row-major tile stride (bf16)
-  static constexpr int TS = kBlk + 8;           // transposed tile stride (bf16)
-  static constexpr int kRow = kBlk * KS * 2;    // bytes of a 32-row tile
-  static constexpr int kTr = D * TS * 2;        // bytes of a transposed tile
   static constexpr int CPR = D / 8;             // 16B chunks per row
   static constexpr int QS = D / 16;             // MFMA steps over the head dim
   static constexpr int DB = D / 32;             // 32-row blocks of a head-dim accumulator
@@ -75,18 +72,6 @@ __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 
 // Position of row i (0..31) in a per-lane-half permuted array of 32 floats:
 // lane half hf reads its 16 rows (in register order) at hf*16.
 __device__ __forceinline__ int perm32(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
-
-// Transposed store of one 16B row chunk: 8 values of row `row`, columns
-// (head dim) c8 .. c8+7, into tile [D][TS] at column slot vslot(row).
-template <int TS>
-__device__ __forceinline__ void store_tr(uint16_t* st, int row, int c8, const u32x4& x) {
-  const int slot = vslot(row);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    st[(c8 + 2 * e) * TS + slot] = (uint16_t)(x[e] & 0xffffu);
-    st[(c8 + 2 * e + 1) * TS + slot] = (uint16_t)(x[e] >> 16);
-  }
-}
 
 __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -326,27 +311,17 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
 // MEM: memory-key units (b*h, memory chunk of 256 keys, query chunk) writing
 // fp32 partials; otherwise window-key units (b*h, window, key chunk of 256)
 // writing the final gradients.  PASS 0: dV; PASS 1: dK.  Each iteration
-// stages kSub blocks of 32 queries (one barrier per kSub blocks) and works
-// through them one after another, so the products of one block can overlap
-// the exponentials of the next.
-constexpr int kSub = 2;
-
-template <int D, int PASS>
-struct DkdvLayout {
-  using T = BT<D>;
-  // per 32-query block: Q rows, then pass 0: dO^T; pass 1: dO rows and Q^T;
-  // then lse and Dv (32 floats each)
-  static constexpr int kMain = PASS == 0 ? T::kRow + T::kTr : 2 * T::kRow + T::kTr;
-  static constexpr int kBlock = kMain + 2 * 32 * 4;
-  static constexpr int kBuf = kSub * kBlock;     // one staging buffer
-};
-
+// takes 64 queries (two blocks of 32, one barrier): the Q and dO tiles are
+// loaded straight into LDS (the dQ kernel's row swizzle); Q rows and dO rows
+// are read as MFMA operands, and dO^T (pass 0) and Q^T (pass 1) with the
+// transposing LDS read.
 template <int D, bool MEM, int PASS>
 __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   using T = BT<D>;
-  using DL = DkdvLayout<D, PASS>;
-  constexpr int kMain = DL::kMain;
-  constexpr int kBuf = DL::kBuf;
+  using Q = DqDma<D>;
+  constexpr int CPR = Q::CPR, RowB = Q::RowB, TB = Q::kTileB;
+  constexpr int kQ = Q::kKeys;                 // queries per iteration
+  constexpr int kBufB = 2 * TB + 2 * kQ * 4;   // Q tile, dO tile, lse and Dv
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int bh, kbase, nq, qbase = 0, win = 0;
   if constexpr (MEM) {
@@ -373,7 +348,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
   const uint32_t stb = (uint32_t)p.stride_tok * 2u;
   const int nkeys = MEM ? p.G : p.m;
-  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBuf);
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBufB);
   if constexpr (!MEM) {
     for (int r = tid; r < p.m; r += kThreads) tab[r] = window_token(p.geo, win, r);
     __syncthreads();
@@ -399,72 +374,64 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
 #pragma unroll
   for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
 
-  constexpr int kIter = kSub * kBlk;   // queries per iteration
-  const int nit = (nq + kIter - 1) / kIter;
-  const int lr = tid / T::CPR, lc = tid % T::CPR;
-  const bool loader = lr < kBlk;
-  u32x4 qx[kSub], dx[kSub];
-  float lx = INFINITY, dvx = 0.0f;
+  const int nit = (nq + kQ - 1) / kQ;
   auto token_of = [&](int q) __attribute__((always_inline)) {
     return MEM ? qbase + q : tab[q];
   };
-  auto load_block = [&](int it) __attribute__((always_inline)) {
-    if (loader) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  float lx = INFINITY, dvx = 0.0f;
+  // this wave's share of the Q and dO tile loads of iteration it; lse and Dv
+  // of the iteration's queries into registers (stored by `put`)
+  auto get = [&](int it) __attribute__((always_inline)) {
+    unsigned char* b = smem + (it & 1) * kBufB;
 #pragma unroll
-      for (int sb = 0; sb < kSub; ++sb) {
-        const int q = min(it * kIter + sb * kBlk + lr, nq - 1);
-        const uint32_t off = (uint32_t)token_of(q) * stb + lc * 16;
-        qx[sb] = buf_load16(make_rsrc(p.q + base), off, 0);
-        dx[sb] = buf_load16(make_rsrc(p.dout + base), off, 0);
-      }
+    for (int i = 0; i < Q::kIpw; ++i) {
+      const int ins = wv * Q::kIpw + i;
+      const int r = (ins * 64 + lane) / CPR;
+      const uint32_t cb = (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
+      const int q = min(it * kQ + r, nq - 1);
+      const uint32_t off = (uint32_t)token_of(q) * stb + cb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.q + base),
+          (__attribute__((address_space(3))) void*)(b + ins * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.dout + base),
+          (__attribute__((address_space(3))) void*)(b + TB + ins * 1024), 16, off, 0, 0, 0);
     }
-    if (tid < kIter) {
-      const int q = it * kIter + tid;
+    if (tid < kQ) {
+      const int q = it * kQ + tid;
       const bool ok = q < nq;
       const int64_t idx = (int64_t)bh * p.n + token_of(ok ? q : nq - 1);
       lx = ok ? p.lse[idx] * kLog2e : INFINITY;   // a missing query gets P = 0
       dvx = ok ? p.dvec[idx] : 0.0f;
     }
   };
-  auto store_block = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* bb = smem + buf * kBuf;
-    if (loader) {
-#pragma unroll
-      for (int sb = 0; sb < kSub; ++sb) {
-        uint16_t* sq = reinterpret_cast<uint16_t*>(bb + sb * DL::kBlock);
-        *reinterpret_cast<u32x4*>(sq + lr * T::KS + lc * 8) = qx[sb];
-        if constexpr (PASS == 0) {
-          store_tr<T::TS>(sq + kBlk * T::KS, lr, lc * 8, dx[sb]);          // dO^T
-        } else {
-          uint16_t* sdo = sq + kBlk * T::KS;
-          *reinterpret_cast<u32x4*>(sdo + lr * T::KS + lc * 8) = dx[sb];   // dO rows
-          store_tr<T::TS>(sdo + kBlk * T::KS, lr, lc * 8, qx[sb]);         // Q^T
-        }
-      }
-    }
-    if (tid < kIter) {
-      float* sl = reinterpret_cast<float*>(bb + (tid / kBlk) * DL::kBlock + kMain);
-      sl[perm32(tid % kBlk)] = lx;
-      sl[32 + perm32(tid % kBlk)] = dvx;
+  auto put = [&](int it) __attribute__((always_inline)) {
+    if (tid < kQ) {
+      float* sl = reinterpret_cast<float*>(smem + (it & 1) * kBufB + 2 * TB);
+      sl[(tid / kBlk) * 64 + perm32(tid % kBlk)] = lx;
+      sl[(tid / kBlk) * 64 + 32 + perm32(tid % kBlk)] = dvx;
     }
   };
-  load_block(0);
-  store_block(0);
+  get(0);
+  put(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
   const float c1 = p.c1;
   const float bias = MEM ? p.mem_bias_raw : 0.0f;
+  const int x = Q::swz(l32);
+  const int sq = (lane & 15) >> 2;
+  const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
   for (int it = 0; it < nit; ++it) {
-    if (it + 1 < nit) load_block(it + 1);
+    if (it + 1 < nit) get(it + 1);
+    const unsigned char* sqt = smem + (it & 1) * kBufB;   // Q tile
+    const unsigned char* sdo = sqt + TB;                  // dO tile
 #pragma unroll
-    for (int sb = 0; sb < kSub; ++sb) {
-      const unsigned char* b = smem + (it & 1) * kBuf + sb * DL::kBlock;
-      const uint16_t* sq = reinterpret_cast<const uint16_t*>(b);
-      const float* sl = reinterpret_cast<const float*>(b + kMain);
+    for (int kb = 0; kb < 2; ++kb) {
+      const float* sl = reinterpret_cast<const float*>(sqt + 2 * TB) + kb * 64;
       f32x16 s{};
 #pragma unroll
       for (int ss = 0; ss < T::QS; ++ss) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sq + l32 * T::KS + hf * (D / 2) + ss * 8);
-        s = mfma(a, kreg[ss], s);
+        const int off = (kb * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16);
+        s = mfma(*reinterpret_cast<const u32x4*>(sqt + off), kreg[ss], s);
       }
       float pr[16];
 #pragma unroll
@@ -474,51 +441,51 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
         for (int i = 0; i < 4; ++i)
           pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i] + bias, c1, -l4[i]));
       }
+      float w[16];   // pass 0: P; pass 1: dS
       if constexpr (PASS == 0) {
-        const uint16_t* sdt = sq + kBlk * T::KS;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 pb{pack_bf16x2(pr[8 * u], pr[8 * u + 1]), pack_bf16x2(pr[8 * u + 2], pr[8 * u + 3]),
-                         pack_bf16x2(pr[8 * u + 4], pr[8 * u + 5]),
-                         pack_bf16x2(pr[8 * u + 6], pr[8 * u + 7])};
-#pragma unroll
-          for (int db = 0; db < T::DB; ++db) {
-            const u32x4 a =
-                *reinterpret_cast<const u32x4*>(sdt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-            acc[db] = mfma(a, pb, acc[db]);
-          }
-        }
+        for (int i = 0; i < 16; ++i) w[i] = pr[i];
       } else {
-        const uint16_t* sdo = sq + kBlk * T::KS;
-        const uint16_t* sqt = sdo + kBlk * T::KS;
         f32x16 dp{};
 #pragma unroll
         for (int ss = 0; ss < T::QS; ++ss) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sdo + l32 * T::KS + hf * (D / 2) + ss * 8);
-          dp = mfma(a, vreg[ss], dp);
+          const int off = (kb * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16);
+          dp = mfma(*reinterpret_cast<const u32x4*>(sdo + off), vreg[ss], dp);
         }
-        float ds[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + hf * 16 + r4 * 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ds[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+          for (int i = 0; i < 4; ++i) w[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
         }
+      }
+      // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS -- the transposed
+      // operand by transposing reads of the row-major tile
+      const unsigned char* tt = PASS == 0 ? sdo : sqt;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 pb{pack_bf16x2(ds[8 * u], ds[8 * u + 1]), pack_bf16x2(ds[8 * u + 2], ds[8 * u + 3]),
-                         pack_bf16x2(ds[8 * u + 4], ds[8 * u + 5]),
-                         pack_bf16x2(ds[8 * u + 6], ds[8 * u + 7])};
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb{pack_bf16x2(w[8 * u], w[8 * u + 1]), pack_bf16x2(w[8 * u + 2], w[8 * u + 3]),
+                       pack_bf16x2(w[8 * u + 4], w[8 * u + 5]), pack_bf16x2(w[8 * u + 6], w[8 * u + 7])};
+        const int slc = 2 * kb + u;
 #pragma unroll
-          for (int db = 0; db < T::DB; ++db) {
-            const u32x4 a =
-                *reinterpret_cast<const u32x4*>(sqt + (db * 32 + l32) * T::TS + u * 16 + hf * 8);
-            acc[db] = mfma(a, pb, acc[db]);
+        for (int db = 0; db < T::DB; ++db) {
+          bf16x4 h2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = 16 * slc + 8 * h + 4 * hf + sq;
+            const int d = 32 * db + d0;
+            h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
+                tt + row * RowB + (((d >> 3) ^ Q::swz(row)) * 16) + (d & 7) * 2));
           }
+          const bf16x8 av = {h2[0][0], h2[0][1], h2[0][2], h2[0][3],
+                             h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pb),
+                                                           acc[db], 0, 0, 0);
         }
       }
     }
-    if (it + 1 < nit) store_block((it + 1) & 1);
+    if (it + 1 < nit) put(it + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next tiles
     __syncthreads();
   }
 
@@ -538,10 +505,10 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
     const int tok = tab[kcl];
     const float* add = nullptr;
     if (p.G > 0) {
-      const int x = tok % p.geo.Wg;
+      const int xx = tok % p.geo.Wg;
       const int y = (tok / p.geo.Wg) % p.geo.Hg;
       const int t = tok / (p.geo.Wg * p.geo.Hg);
-      const int cell = ((t / p.pt) * p.Gy + y / p.py) * p.Gx + x / p.px;
+      const int cell = ((t / p.pt) * p.Gy + y / p.py) * p.Gx + xx / p.px;
       add = (PASS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
     }
     store_rows<D>(acc, PASS == 0 ? 1.0f : p.scale, add, (PASS == 0 ? p.dv : p.dk) + base,
@@ -586,8 +553,7 @@ int set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MEM>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
-  const size_t lds = 2 * (size_t)max(DkdvLayout<D, 0>::kBuf, DkdvLayout<D, 1>::kBuf) +
-                     (MEM ? 0 : (size_t)p.m * 4);
+  const size_t lds = 2 * (2 * (size_t)DqDma<D>::kTileB + 2 * 64 * 4) + (MEM ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
   const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + kUnit - 1) / kUnit) * p.nqc
                             : (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
