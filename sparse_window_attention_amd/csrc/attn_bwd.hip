@@ -209,6 +209,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
     const int k0 = it * Q::kKeys;
     unsigned char* bk = smem + (it & 1) * KTB;
     unsigned char* bv = smem + (2 + (it & 1)) * KTB;
+    const bool winT = k0 + Q::kKeys <= p.m;
+    const bool memT = k0 >= p.m && k0 + Q::kKeys <= L;
+    // window tiles: all table reads first (one LDS wait), then the loads
+    uint32_t toff[Q::kIpw];
+#pragma unroll
+    for (int i = 0; i < Q::kIpw; ++i) {
+      const int r = ((wv * Q::kIpw + i) * 64 + lane) / CPR;
+      toff[i] = winT ? (uint32_t)tab[k0 + r] * stb : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < Q::kIpw; ++i) {
       const int ins = wv * Q::kIpw + i;
@@ -216,11 +225,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
       const uint32_t cb = (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
       auto* lk = (__attribute__((address_space(3))) void*)(bk + ins * 1024);
       auto* lv = (__attribute__((address_space(3))) void*)(bv + ins * 1024);
-      if (k0 + Q::kKeys <= p.m) {
-        const uint32_t off = (uint32_t)tab[k0 + r] * stb + cb;
+      if (winT) {
+        const uint32_t off = toff[i] + cb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.k + base), lk, 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.v + base), lv, 16, off, 0, 0, 0);
-      } else if (k0 >= p.m && k0 + Q::kKeys <= L) {
+      } else if (memT) {
         const uint32_t off = (uint32_t)(k0 - p.m + r) * (D * 2) + cb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kmem), lk, 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vmem), lv, 16, off, 0, 0, 0);
@@ -384,13 +393,18 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   // of the iteration's queries into registers (stored by `put`)
   auto get = [&](int it) __attribute__((always_inline)) {
     unsigned char* b = smem + (it & 1) * kBufB;
+    // all row tokens first (one LDS wait for the window table), then the loads
+    int tok[Q::kIpw];
+#pragma unroll
+    for (int i = 0; i < Q::kIpw; ++i) {
+      const int r = ((wv * Q::kIpw + i) * 64 + lane) / CPR;
+      tok[i] = token_of(min(it * kQ + r, nq - 1));
+    }
 #pragma unroll
     for (int i = 0; i < Q::kIpw; ++i) {
       const int ins = wv * Q::kIpw + i;
       const int r = (ins * 64 + lane) / CPR;
-      const uint32_t cb = (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
-      const int q = min(it * kQ + r, nq - 1);
-      const uint32_t off = (uint32_t)token_of(q) * stb + cb;
+      const uint32_t off = (uint32_t)tok[i] * stb + (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.q + base),
           (__attribute__((address_space(3))) void*)(b + ins * 1024), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.dout + base),
