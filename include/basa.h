@@ -41,6 +41,10 @@
  *     enqueues work and returns; it never synchronises the stream.
  *   - Ownership: the caller owns every buffer.  The library allocates no
  *     device memory and holds no state between calls (reentrant).
+ *   - Empty batches: batch or heads may be 0.  Such a call has nothing to
+ *     do: it returns BASA_OK once head_dim, dtype and layout are valid,
+ *     reads no pointer (they may be NULL, as an empty tensor's are) and
+ *     launches nothing.
  *   - Errors: every call returns a status.  Arguments are validated before
  *     anything is enqueued; on any error nothing is launched and no output
  *     byte is written.  basa_last_error() gives a sentence naming the
@@ -108,7 +112,7 @@ int basa_shift_for_block(int32_t block_idx, int32_t schedule, int32_t ndim,
  * Accumulates in fp32 and stores in dtype (bf16 rounded to nearest even).
  *   k, v          device, B x H x n x D in `layout`, n = prod(grid)
  *   k_mem, v_mem  device, [B, H, G, D] contiguous, G = basa_mem_tokens()
- *   batch, heads  >= 1;  head_dim in {64, 128}
+ *   batch, heads  >= 0 (0: an empty batch);  head_dim in {64, 128}
  *   ndim, grid, pool  host arrays of ndim entries; pool must divide grid
  * Errors: INVALID_ARG (NULL, bad dims, pool not dividing the grid, an output
  * overlapping an input or the other output), UNSUPPORTED (dtype, head_dim).

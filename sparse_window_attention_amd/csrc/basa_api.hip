@@ -82,7 +82,7 @@ int check_divides(int32_t ndim, const int32_t* part, const int32_t g[3], int32_t
 }
 
 int check_common(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, int32_t layout) {
-  if (batch <= 0 || heads <= 0) return fail(BASA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (batch < 0 || heads < 0) return fail(BASA_ERR_INVALID_ARG, "batch and heads must be >= 0");
   if ((int64_t)batch * heads > INT32_MAX / 2) return fail(BASA_ERR_UNSUPPORTED, "batch*heads too large");
   if (dtype != BASA_BF16 && dtype != BASA_F32) return fail(BASA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (head_dim != 64 && head_dim != 128)
@@ -90,6 +90,16 @@ int check_common(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, 
   if (layout != BASA_LAYOUT_BHND && layout != BASA_LAYOUT_BNHD)
     return fail(BASA_ERR_INVALID_ARG, "unknown layout %d", layout);
   return BASA_OK;
+}
+
+// An empty batch (batch or heads 0) is a call with nothing to do: once the
+// scalar arguments are valid it succeeds without reading any pointer, so
+// empty tensors (whose data pointers may be NULL) pass through.  Returns -1
+// when the batch is not empty, else the status to return.
+int empty_call(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, int32_t layout) {
+  if (batch != 0 && heads != 0) return -1;
+  const int rc = check_common(batch, heads, head_dim, dtype, layout);
+  return rc ? rc : ok();
 }
 
 // Strides (elements) of a B x H x n x D tensor in the given layout.
@@ -166,6 +176,7 @@ int basa_pool_kv(const void* k, const void* v, void* k_mem, void* v_mem, int32_t
                  int32_t heads, int32_t head_dim, int32_t ndim, const int32_t* grid,
                  const int32_t* pool, int32_t dtype, int32_t layout, void* stream) {
   try {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!k || !v || !k_mem || !v_mem) return fail(BASA_ERR_INVALID_ARG, "k, v, k_mem and v_mem must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
@@ -210,6 +221,7 @@ int window_attn_impl(const void* q, const void* k, const void* v, const void* k_
                      const int32_t* window, const int32_t* shift, float scale, float mem_bias,
                      int32_t dtype, int32_t layout, void* stream) {
   {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
@@ -365,6 +377,7 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
                          const int32_t* pool, float scale, float mem_bias, int32_t dtype,
                          int32_t layout, void* stream) {
   try {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
       return fail(BASA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
@@ -495,6 +508,7 @@ int basa_gather_kv(const void* k, const void* v, const int32_t* idx, int64_t n_i
                    void* v_out, int32_t batch, int32_t heads, int32_t head_dim, int64_t n_tokens,
                    int32_t dtype, int32_t layout, void* stream) {
   try {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!k || !v || !idx || !k_out || !v_out)
       return fail(BASA_ERR_INVALID_ARG, "k, v, idx, k_out and v_out must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
@@ -532,6 +546,7 @@ int basa_curve_attn(const void* q, const void* k, const void* v, const void* k_m
                     int64_t slide, float scale, float mem_bias, int32_t dtype, int32_t layout,
                     void* stream) {
   try {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!q || !k || !v || !out || !order)
       return fail(BASA_ERR_INVALID_ARG, "q, k, v, out and order must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
@@ -607,6 +622,7 @@ int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32
                    int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
                    int32_t layout, void* stream) {
   try {
+    if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;

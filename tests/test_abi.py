@@ -100,7 +100,7 @@ def _win(**kw):
     (dict(out=FAKE + 64), S.BASA_ERR_INVALID_ARG),                  # out overlaps q
     (dict(km=FAKE + 4 * SZ, vm=FAKE + 3 * SZ + 256, G=4), S.BASA_ERR_INVALID_ARG),  # out overlaps v_mem
     (dict(q=FAKE + 8), S.BASA_ERR_INVALID_ARG),                     # misaligned
-    (dict(B=0), S.BASA_ERR_INVALID_ARG),
+    (dict(B=-1), S.BASA_ERR_INVALID_ARG),
     (dict(layout=5), S.BASA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), S.BASA_ERR_INVALID_ARG),
     (dict(bias=float("inf")), S.BASA_ERR_INVALID_ARG),
@@ -284,3 +284,25 @@ def test_calib_mfma_validation():
     assert S.lib.basa_calib_mfma(None, 4, 10, None) == S.BASA_ERR_INVALID_ARG
     assert S.lib.basa_calib_mfma(FAKE, 0, 10, None) == S.BASA_ERR_INVALID_ARG
     assert S.lib.basa_calib_mfma(FAKE, 4, 0, None) == S.BASA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    # batch or heads 0: BASA_OK without reading any pointer (all NULL here),
+    # once head_dim, dtype and layout are valid
+    arr = S._arr
+    for B, H in ((0, 2), (1, 0), (0, 0)):
+        assert _win(q=None, k=None, v=None, out=None, B=B, H=H) == S.BASA_OK
+        assert S.lib.basa_pool_kv(None, None, None, None, B, H, 128, 2, arr((8, 8)), arr((4, 4)),
+                                  S.BASA_BF16, 0, None) == S.BASA_OK
+        assert S.lib.basa_full_attn(None, None, None, None, B, H, 64, 128, -1.0, S.BASA_BF16, 0,
+                                    None) == S.BASA_OK
+        assert S.lib.basa_gather_kv(None, None, None, 4, None, None, B, H, 128, 64, S.BASA_BF16, 0,
+                                    None) == S.BASA_OK
+        assert S.lib.basa_curve_attn(None, None, None, None, None, 0, None, B, H, 128, 64, None, 16,
+                                     0, -1.0, 0.0, S.BASA_BF16, 0, None) == S.BASA_OK
+        assert _bwd(q=None, k=None, v=None, km=None, vm=None, out=None, dout=None, lse=None,
+                    dq=None, dk=None, dv=None, ws=None, B=B, H=H) == S.BASA_OK
+    # the scalar arguments are still checked
+    assert _win(q=None, k=None, v=None, out=None, B=0, D=96) == S.BASA_ERR_UNSUPPORTED
+    assert _win(q=None, k=None, v=None, out=None, B=0, dtype=7) == S.BASA_ERR_UNSUPPORTED
+    assert _win(q=None, k=None, v=None, out=None, B=0, layout=3) == S.BASA_ERR_INVALID_ARG

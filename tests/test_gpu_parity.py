@@ -302,3 +302,18 @@ def test_binding_errors_before_launch():
         S.window_attn(x, x, x.clone(), (8, 8), (3, 8), (0, 0))
     with pytest.raises(S.BasaError):
         S.window_attn(x, x, x, (8, 8), (4, 4), (0, 0), out=x)    # out aliases q
+
+
+def test_empty_batch():
+    # zero-sized batch: every call succeeds through the C ABI and returns empty outputs
+    log("empty batch")
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.empty((0, 3, 64, 128), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    mem = S.pool_kv(k, v, (8, 8), (4, 4))
+    assert tuple(mem[0].shape) == (0, 3, 4, 128)
+    out = S.window_attn(q, k, v, (8, 8), (4, 4), (2, 2), mem=mem)
+    assert tuple(out.shape) == (0, 3, 64, 128)
+    assert tuple(S.full_attn(q, k, v).shape) == (0, 3, 64, 128)
+    order = torch.arange(64, dtype=torch.int32, device=dev)
+    assert tuple(S.curve_attn(q, k, v, order, 16, 3).shape) == (0, 3, 64, 128)
+    _sync()
