@@ -165,6 +165,21 @@ def test_flux2048_sampled(wl):
         _sampled_check(wl, shift, heads=[0, 13, 23], windows=sample_windows(wl.n_windows))
 
 
+NOMEM = [W.FLUX2048_W16.with_(name="flux2048_128x128_w16_nomem", pool=None),
+         W.FLUX2048_W32.with_(name="flux2048_128x128_w32_nomem", pool=None)]
+
+
+@pytest.mark.parametrize("wl", NOMEM, ids=lambda w: w.name)
+def test_flux2048_no_memory_sampled(wl):
+    # 4 (w16) and 16 (w32) key tiles per unit and several units per
+    # workgroup: the persistent kernel's shortest units, whose successor's
+    # tile loads start in their second iteration
+    for block in (1, 3):
+        shift = S.shift_for_block(block, wl.schedule, wl.window)
+        log(f"{wl.name} block={block} shift={shift}")
+        _sampled_check(wl, shift, heads=[0, 23], windows=sample_windows(wl.n_windows))
+
+
 @pytest.mark.parametrize("wl", [W.WAN, W.WAN_G1638], ids=lambda w: w.name)
 def test_wan_sampled(wl):
     for block in range(2):
