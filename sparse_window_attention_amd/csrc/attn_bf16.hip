@@ -47,6 +47,14 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
 constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel needs
+// Persistent kernel: LDS operand reads this many MFMA steps ahead (score
+// product, P V product).
+#ifndef BASA_OPERAND_AHEAD
+#define BASA_OPERAND_AHEAD 2
+#endif
+#ifndef BASA_OPERAND_AHEAD_PV
+#define BASA_OPERAND_AHEAD_PV BASA_OPERAND_AHEAD
+#endif
 // Persistent kernel: waves per workgroup and workgroups per CU.
 #ifndef BASA_PERSISTENT_WAVES
 #define BASA_PERSISTENT_WAVES 8
@@ -361,26 +369,27 @@ struct Core {
     constexpr int H = TL::CPR / 2;
     const int x = swz_k(l32);
     const uint32_t kbase = (uint32_t)(l32 * (TL::CPR * 16) + 16 * ((hf * H) ^ (x & H)) + 16 * (x & (H - 1)));
-    // operands of step ss+1 are read before the products of step ss
-    u32x4 a[2][KB];
+    // operands are read kAhead steps before their products
+    constexpr int kAhead = BASA_OPERAND_AHEAD;
+    u32x4 a[kAhead + 1][KB];
+    auto rd = [&](int ss, int slot) __attribute__((always_inline)) {
+      const uint32_t off = kbase ^ (uint32_t)(16 * ss);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      a[0][kb] = *reinterpret_cast<const u32x4*>(kt + kbase + kb * 32 * (TL::CPR * 16));
+      for (int kb = 0; kb < KB; ++kb)
+        a[slot][kb] = *reinterpret_cast<const u32x4*>(kt + off + kb * 32 * (TL::CPR * 16));
+    };
+#pragma unroll
+    for (int i = 0; i < kAhead && i < QS; ++i) rd(i, i);
 #pragma unroll
     for (int ss = 0; ss < QS; ++ss) {
-      if (ss + 1 < QS) {
-        const uint32_t off = kbase ^ (uint32_t)(16 * (ss + 1));
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          a[(ss + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(kt + off + kb * 32 * (TL::CPR * 16));
-      }
+      if (ss + kAhead < QS) rd(ss + kAhead, (ss + kAhead) % (kAhead + 1));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[ss & 1][kb]), __builtin_bit_cast(bf16x8, qreg[qb][ss]),
-              ss == 0 ? zero16 : s[qb][kb], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, a[ss % (kAhead + 1)][kb]),
+              __builtin_bit_cast(bf16x8, qreg[qb][ss]), ss == 0 ? zero16 : s[qb][kb], 0, 0, 0);
       }
     }
   }
@@ -409,16 +418,18 @@ struct Core {
             vt + vb + (16 * sl + 8 * h) * (TL::CPR * 16)));
       return bf16x8{h2[0][0], h2[0][1], h2[0][2], h2[0][3], h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
     };
-    bf16x8 av[2];
-    av[0] = rd(0);
+    constexpr int kAhead = BASA_OPERAND_AHEAD_PV;
+    bf16x8 av[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead && i < NP; ++i) av[i] = rd(i);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (i + 1 < NP) av[(i + 1) & 1] = rd(i + 1);
+      if (i + kAhead < NP) av[(i + kAhead) % (kAhead + 1)] = rd(i + kAhead);
       const int db = i / (2 * KB), sl = i % (2 * KB);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            av[i & 1], __builtin_bit_cast(bf16x8, pb[qb][sl]), acc[qb][db], 0, 0, 0);
+            av[i % (kAhead + 1)], __builtin_bit_cast(bf16x8, pb[qb][sl]), acc[qb][db], 0, 0, 0);
     }
   }
 
