@@ -406,10 +406,11 @@ struct Core {
     const int sq = (lane & 15) >> 2;       // row within the 4-row group
     const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
     const uint32_t lanev = (uint32_t)((4 * hf + sq) * (TL::CPR * 16) + (d0 & 7) * 2);
-    // operands of product i+1 are read before product i
+    // product i is (d block i % DB, key slice i / DB): consecutive products
+    // update different accumulators
     constexpr int NP = DB * 2 * KB;
     auto rd = [&](int i) __attribute__((always_inline)) {
-      const int db = i / (2 * KB), sl = i % (2 * KB);
+      const int db = i % DB, sl = i / DB;
       const uint32_t vb = lanev + (uint32_t)((((4 * db + (d0 >> 3)) ^ swz_v(sq)) * 16));
       bf16x4 h2[2];
 #pragma unroll
@@ -425,7 +426,7 @@ struct Core {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + kAhead < NP) av[(i + kAhead) % (kAhead + 1)] = rd(i + kAhead);
-      const int db = i / (2 * KB), sl = i % (2 * KB);
+      const int db = i % DB, sl = i / DB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -524,12 +525,13 @@ struct Core {
       }
     }
   }
-  // P = exp2(S*c1 - m): row sums (two partial sums) and the bf16 operands of
-  // the P V product
-  __device__ __forceinline__ void make_p(const Scores& s, Probs& pb) {
+  // P = exp2(S*c1 + off - m): row sums (two partial sums) and the bf16
+  // operands of the P V product.  off is a logit offset (log2 units) shared
+  // by every key of the tile.
+  __device__ __forceinline__ void make_p(const Scores& s, Probs& pb, float off = 0.0f) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float nm = -m_used[qb];
+      const float nm = off - m_used[qb];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -780,7 +782,19 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
   C c(p, smem);
   // even tile count; a padding tile holds only keys >= L, which the mask removes
   const int nkt = (c.nkt + 1) & ~1;
-  if (nkt != c.nkt) c.tmask = min(c.tmask, c.nkt);
+  // Per-key masking (the memory bias per key, padding keys to -inf) starts
+  // at the tile that straddles the window / memory boundary or holds
+  // padding keys.  Tiles of memory keys only before that take the bias as
+  // one offset of the tile's row max and exponent instead.
+  {
+    int tm = nkt;
+    if (c.bias != 0.0f && c.m % kKT != 0) tm = c.m / kKT;
+    if (c.L % kKT) tm = min(tm, c.nkt - 1);
+    c.tmask = min(tm, c.nkt);
+  }
+  auto bias_of = [&](int t) __attribute__((always_inline)) {
+    return (t < c.tmask && t * kKT >= c.m) ? c.bias : 0.0f;
+  };
   unsigned char* tables = smem + PL::tileBytes;
   // DMA tile buffers: K buffer b at b * kTileB, V buffer b at (2 + b) * kTileB
   auto dK = [&](int b) __attribute__((always_inline)) { return smem + b * C::kTileB; };
@@ -884,6 +898,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       float mx[1];
       if (c.tmask == 0) c.mask_s(sA, 0);
       c.rowmax_all(sA, mx);
+      mx[0] += bias_of(0);
       c.update_max(mx);
     }
     if constexpr (!DMA) {
@@ -905,11 +920,12 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       Probs pb;
       float mxn[1];
       scores((t + 1) & 1, sn);
-      c.make_p(sc, pb);
+      c.make_p(sc, pb, bias_of(t) * c.c1);
       if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
       else c.pv(c.sV(t & 1), pb);
       if constexpr (decltype(masked)::value) c.mask_s(sn, (t + 1) * kKT);
       c.rowmax_all(sn, mxn);
+      mxn[0] += bias_of(t + 1);
       if constexpr (DMA) {
         wait_vmem();  // this wave's loads of V(t+1) and K(t+2)
       } else {
@@ -967,7 +983,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     }
     {
       Probs pb;
-      c.make_p(sA, pb);
+      c.make_p(sA, pb, bias_of(t) * c.c1);
       if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
       else c.pv(c.sV(t & 1), pb);
     }
