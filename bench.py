@@ -131,6 +131,59 @@ def time_steps(S, wl, sets, steps, warmup, stream, with_mem=True):
     return total / steps, pool, attn
 
 
+def time_steps_graph(S, wl, sets, steps, warmup, stream, with_mem=True):
+    """The same steps as time_steps, each replayed from a HIP graph captured
+    per (input set, shift phase), with no events between the kernels: the
+    whole-step time without host launches or per-kernel instrumentation.
+    Each graph's output is checked bit for bit against an eager run of the
+    same step (the kernels are deterministic).  Returns (ms/step, ok)."""
+    import torch
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    G = wl.mem_tokens
+    dev = sets[0][0].device
+    outs = [torch.empty_like(s[0]) for s in sets]
+    mems = [(torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev)) for _ in sets]
+    period = len(sets) * 4 // math.gcd(len(sets), 4)
+
+    def step(i, out=None):
+        si = i % len(sets)
+        q, k, v = sets[si]
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        mem = S.pool_kv(k, v, wl.grid, wl.pool, out=mems[si]) if with_mem else None
+        S.window_attn(q, k, v, wl.grid, wl.window, shift, mem=mem,
+                      out=outs[si] if out is None else out)
+
+    for i in range(max(warmup, period)):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(period):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # every graph against the eager step, with eager work and syncs between
+    ok = True
+    ref = torch.empty_like(outs[0])
+    for i in range(period):
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        step(i, out=ref)
+        torch.cuda.synchronize()
+        ok = ok and torch.equal(outs[i % len(sets)], ref)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        graphs[i % period].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, ok
+
+
 def time_dense(S, sets, reps, stream):
     import torch
     q, k, v = sets[0]
@@ -550,7 +603,11 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
     n, m, G, D, H, B = (wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.heads,
                        wl.batch)
     sets = make_sets(wl, args.sets, dev)
-    ms_step, pool, attn = time_steps(S, wl, sets, args.steps, args.warmup, stream, True)
+    # per-kernel times from eager steps with events around each kernel; the
+    # step time from graph-replayed steps without them
+    ms_eager, pool, attn = time_steps(S, wl, sets, args.steps, args.warmup, stream, True)
+    ms_graph, graph_ok = time_steps_graph(S, wl, sets, args.steps, args.warmup, stream, True)
+    ms_step = ms_graph if graph_ok else ms_eager
     flops = window_flops(B, H, n, m, G, D)
     flops_nomem = window_flops(B, H, n, m, 0, D)
     attn_bytes = 4 * B * H * n * D * 2 + 2 * B * H * G * D * 2
@@ -561,6 +618,9 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
         "workload": wl.name, "n": n, "m": m, "G": G,
         "ms_per_step": ms_step,
         "tflops_per_step": flops / (ms_step * 1e-3) / 1e12,
+        "step_launch": "hip graph per step" if graph_ok else "eager",
+        "graph_output_equals_eager": graph_ok,
+        "ms_per_step_eager_with_events": ms_eager,
         "window_attn_ms": {"mean": attn_ms, "median": median(attn), "p10": pct(attn, 10),
                            "p90": pct(attn, 90)},
         "pool_kv_ms": {"mean": pool_ms, "median": median(pool)},
@@ -646,8 +706,10 @@ def main():
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
         ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)
-        print(json.dumps({"ms_per_step": ms, "attn_ms": sum(attn) / len(attn),
-                          "pool_ms": sum(pool) / len(pool)}))
+        ms_g, ok = time_steps_graph(S, head, sets, args.steps, args.warmup, stream, True)
+        print(json.dumps({"ms_per_step": ms_g if ok else ms, "graph_output_equals_eager": ok,
+                          "ms_per_step_eager_with_events": ms,
+                          "attn_ms": sum(attn) / len(attn), "pool_ms": sum(pool) / len(pool)}))
         return
     res = measure_window(S, head, args, stream, dev)
     print(f"[bench] {head.name}: attn {res['window_attn_ms']['mean']*1e3:.1f} us "
@@ -724,7 +786,8 @@ def main():
                    "heads": head.heads, "head_dim": head.head_dim, "grid": list(head.grid),
                    "window": list(head.window), "pool": list(head.pool),
                    "mem_tokens": head.mem_tokens, "schedule": "four-phase",
-                   "input_sets_rotated": args.sets, "parallelism": "none (1 GPU)"},
+                   "input_sets_rotated": args.sets, "step_launch": res["step_launch"],
+                   "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "ms_per_attn_call": res["window_attn_ms"]["mean"],
         "windows": {f"{res['m']}": res, f"{res_o['m']}": res_o},
