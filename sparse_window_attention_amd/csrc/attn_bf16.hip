@@ -793,7 +793,8 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     c.tmask = min(tm, c.nkt);
   }
   auto bias_of = [&](int t) __attribute__((always_inline)) {
-    return (t < c.tmask && t * kKT >= c.m) ? c.bias : 0.0f;
+    if constexpr (FULL) return 0.0f;  // no memory keys
+    else return (t < c.tmask && t * kKT >= c.m) ? c.bias : 0.0f;
   };
   unsigned char* tables = smem + PL::tileBytes;
   // DMA tile buffers: K buffer b at b * kTileB, V buffer b at (2 + b) * kTileB
