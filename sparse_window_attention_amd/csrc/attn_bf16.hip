@@ -27,8 +27,8 @@
 // transposing LDS read.  While a unit runs, the next unit's first three K/V
 // tiles are loaded into free tile buffers and its Q rows into a per-wave LDS
 // staging area, so the next unit starts from LDS instead of paying a burst
-// of HBM loads, and the finished unit's output stores drain while the next
-// one computes.
+// of HBM loads; the finished unit's output is stored once the next unit's
+// first scores are formed.
 //
 // The cyclic shift and the window gather are address arithmetic: a table of
 // the window's raster offsets is built in LDS per unit and every Q/K/V/O row
