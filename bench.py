@@ -637,6 +637,16 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
         "flops_per_call": flops, "attn_bytes_per_call": attn_bytes,
         "pool_bytes_per_call": pool_bytes,
     }
+    # hot cache (secondary): every step on the first input set, so much of
+    # Q, K and V (302 MB at FLUX-2048) stays in the 256 MB last-level cache
+    ms_hot, pool_hot, attn_hot = time_steps(S, wl, sets[:1], max(10, args.steps // 2), 3, stream,
+                                            True)
+    r["hot_one_input_set"] = {
+        "ms_per_step_eager_with_events": ms_hot,
+        "window_attn_ms": sum(attn_hot) / len(attn_hot),
+        "pool_kv_ms": sum(pool_hot) / len(pool_hot),
+        "window_attn_tflops": flops / (sum(attn_hot) / len(attn_hot) * 1e-3) / 1e12,
+    }
     # memory off: the literal n/m comparison
     _, _, attn0 = time_steps(S, wl, sets, max(10, args.steps // 2), 3, stream, False)
     attn0_ms = sum(attn0) / len(attn0)
