@@ -375,6 +375,37 @@ def cpu_baseline(wl, target_s):
             "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
 
 
+def oracle_per_config():
+    """The oracle beside the other shapes: one head of FLUX-1024, Wan and
+    Ultra timed (block 1 of the schedule, pool included), the call's time
+    extrapolated to all heads; Tiny by the brute-force masked definition."""
+    import oracle as O
+    import workloads as W
+    res = {}
+    for wl in (W.FLUX1024, W.WAN, W.ULTRA):
+        q, k, v = (W.head_values(wl, t, 0) for t in range(3))
+        shift = O.shift_for_block(1, wl.schedule, wl.window)
+        t0 = time.perf_counter()
+        km = O.pool_mean(k[None, None], wl.grid, wl.pool)[0, 0]
+        vm = O.pool_mean(v[None, None], wl.grid, wl.pool)[0, 0]
+        O.window_attention_head(q, k, v, wl.grid, wl.window, shift, km, vm)
+        dt = time.perf_counter() - t0
+        fl = O.window_flops(1, 1, wl.n_tokens, wl.window_tokens, wl.mem_tokens, wl.head_dim)
+        res[wl.name] = {"ms_one_head": dt * 1e3,
+                        "ms_per_call_extrapolated": dt * 1e3 * wl.heads * wl.batch,
+                        "tflops": fl / dt / 1e12,
+                        "note": f"one of {wl.heads} heads timed; the call extrapolated"}
+        del q, k, v, km, vm
+    wl = W.TINY
+    q, k, v = W.make_qkv(wl)
+    shift = (4, 4)
+    t0 = time.perf_counter()
+    O.masked_attention_bruteforce(q, k, v, wl.grid, wl.window, shift)
+    res[wl.name] = {"ms_per_call": (time.perf_counter() - t0) * 1e3,
+                    "note": "brute-force masked attention, the whole call (one head)"}
+    return res
+
+
 def window_permutation(grid, window, shift, device):
     """Raster index of every token in window-major order under the shifted
     partition: windows in raster order of the window grid, tokens in raster
@@ -816,6 +847,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
+        line["cpu_baseline"]["other_configs"] = oracle_per_config()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
