@@ -661,6 +661,11 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
         "window_attn_ms": {"mean": attn_ms, "median": median(attn), "p10": pct(attn, 10),
                            "p90": pct(attn, 90)},
         "pool_kv_ms": {"mean": pool_ms, "median": median(pool)},
+        # timed step i runs schedule phase (warmup + i) mod 4
+        "window_attn_ms_by_phase": {
+            str(ph): sum(a for i, a in enumerate(attn) if (args.warmup + i) % 4 == ph)
+            / max(1, sum(1 for i in range(len(attn)) if (args.warmup + i) % 4 == ph))
+            for ph in range(4)},
         "window_attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
         "window_attn_mfma_frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "window_attn_gbs": attn_bytes / (attn_ms * 1e-3) / 1e9,
