@@ -100,6 +100,37 @@ def test_token_count_corrected_memory(dtype):
     assert_close(to_np(out), ref, dtype, f"mem bias {dtype}")
 
 
+# Persistent kernel (at least four key tiles per unit) with a memory logit
+# bias: tiles of memory keys only take the bias as one offset of the row max
+# and the exponent; a tile straddling the window/memory boundary or holding
+# padding keys takes it per key.
+BIAS_PERSISTENT = [
+    # grid, window, pool: m = 256 with G = 256 (four memory-only tiles) and
+    # G = 80 (one memory-only tile, then one with padding keys); m = 400
+    # with G = 80 (a tile straddling window and memory keys, padding keys)
+    ((64, 64), (16, 16), (4, 4)),
+    ((64, 80), (16, 16), (8, 8)),
+    ((40, 80), (20, 20), (5, 8)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BIAS_PERSISTENT)))
+def test_memory_bias_persistent(case):
+    grid, window, pool = BIAS_PERSISTENT[case]
+    n, B, H, D = int(np.prod(grid)), 1, 3, 128
+    shift = (window[0] // 2, 3)
+    bias = math.log(float(np.prod(pool)))
+    log(f"memory bias, persistent: grid={grid} window={window} pool={pool}")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=500 + case)
+    qg, kg, vg = (to_gpu(x, "bf16") for x in (q, k, v))
+    mem = S.pool_kv(kg, vg, grid, pool)
+    out = S.window_attn(qg, kg, vg, grid, window, shift, mem=mem, mem_bias=bias)
+    _sync()
+    ref = O.window_attention(q, k, v, grid, window, shift, O.pool_mean(k, grid, pool),
+                             O.pool_mean(v, grid, pool), mem_logit_bias=bias)
+    assert_close(to_np(out), ref, "bf16", f"mem bias persistent case {case}")
+
+
 # ------------------------------------------------------------------ pooling
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
