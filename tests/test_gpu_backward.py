@@ -46,6 +46,9 @@ CASES = [
     ("query chunks", 1, 2, 128, (32, 48), (16, 16), (8, 8), (8, 8), 0.0, "bhnd"),
     ("window 400", 1, 2, 128, (40, 40), (20, 20), (10, 7), (8, 8), 0.0, "bhnd"),
     ("memory 1024", 1, 2, 128, (64, 64), (16, 16), (8, 8), (2, 2), 0.0, "bhnd"),
+    # the persistent forward with memory-only tiles taking the bias as an offset
+    ("memory-only tiles, bias", 1, 2, 128, (64, 64), (16, 16), (8, 3), (4, 4),
+     math.log(16.0), "bhnd"),
 ]
 
 
