@@ -278,6 +278,23 @@ def test_full_attn_many_units():
     assert_close(got, ref, "bf16", "full many units")
 
 
+def test_full_attn_flux2048_sampled():
+    """The dense kernel at the shape the speedup is measured on (24 heads of
+    16384 tokens, D = 128): sampled query rows of two seeded heads."""
+    wl = W.FLUX2048_W16
+    heads = [5, 18]
+    log(f"dense {wl.name} heads {heads}")
+    (qg, kg, vg), exact = make_full_inputs(wl, heads)
+    out = S.full_attn(qg, kg, vg)
+    _sync()
+    rows = np.unique(np.linspace(0, wl.n_tokens - 1, 80).astype(np.int64))
+    for h in heads:
+        q, k, v = exact[h]
+        ref = O.full_attention(q[None, None], k[None, None], v[None, None], rows=rows)[0, 0]
+        got = to_np(out[0, h][torch.from_numpy(rows).to(out.device)])
+        assert_close(got, ref, "bf16", f"dense {wl.name} head {h}")
+
+
 # ------------------------------------------------------------- dense kernel
 @pytest.mark.parametrize("dtype,n,D", [("bf16", 4096, 128), ("bf16", 1000, 128),
                                        ("bf16", 777, 64), ("f32", 300, 64), ("f32", 520, 128)])
