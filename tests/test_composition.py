@@ -28,6 +28,7 @@ def test_window_permutation_matches_oracle_index(grid, window, shift):
 @pytest.mark.parametrize("grid,window,pool,shift", [
     ((32, 48), (16, 16), (8, 8), (8, 5)),
     ((6, 10, 26), (3, 5, 13), (3, 5, 2), (1, 3, 7)),
+    ((128, 128), (16, 16), (8, 8), (8, 8)),     # the FLUX-2048 grid the benchmark times
 ])
 def test_composition_equals_fused(grid, window, pool, shift):
     S = pytest.importorskip("sparse_window_attention_amd")
