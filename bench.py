@@ -643,7 +643,12 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
     # per-kernel times from eager steps with events around each kernel; the
     # step time from graph-replayed steps without them
     ms_eager, pool, attn = time_steps(S, wl, sets, args.steps, args.warmup, stream, True)
-    ms_graph, graph_ok = time_steps_graph(S, wl, sets, args.steps, args.warmup, stream, True)
+    try:
+        ms_graph, graph_ok = time_steps_graph(S, wl, sets, args.steps, args.warmup, stream, True)
+    except Exception as e:  # a runtime without graph capture: report the eager time
+        print(f"[bench] graph replay unavailable ({type(e).__name__}: {e}); eager step time",
+              file=sys.stderr, flush=True)
+        ms_graph, graph_ok = None, False
     ms_step = ms_graph if graph_ok else ms_eager
     flops = window_flops(B, H, n, m, G, D)
     flops_nomem = window_flops(B, H, n, m, 0, D)
@@ -758,7 +763,10 @@ def main():
     if args.only == "window":
         sets = make_sets(head, args.sets, dev)
         ms, pool, attn = time_steps(S, head, sets, args.steps, args.warmup, stream, True)
-        ms_g, ok = time_steps_graph(S, head, sets, args.steps, args.warmup, stream, True)
+        try:
+            ms_g, ok = time_steps_graph(S, head, sets, args.steps, args.warmup, stream, True)
+        except Exception:
+            ms_g, ok = None, False
         print(json.dumps({"ms_per_step": ms_g if ok else ms, "graph_output_equals_eager": ok,
                           "ms_per_step_eager_with_events": ms,
                           "attn_ms": sum(attn) / len(attn), "pool_ms": sum(pool) / len(pool)}))
