@@ -359,6 +359,38 @@ def test_deterministic_and_shift_period():
     assert not torch.equal(a, z0)
 
 
+def test_concurrent_streams():
+    """Calls on two streams at once (default priority) give the results of the
+    same calls made one after the other: the library keeps no state shared
+    between calls."""
+    grid, window, pool = (64, 64), (16, 16), (8, 8)
+    n, B, H, D = 4096, 1, 8, 128
+    log("two streams")
+    ins = []
+    for seed in (900, 901):
+        q, k, v = random_qkv((B, H, n, D), "bf16", seed=seed)
+        ins.append(tuple(to_gpu(x, "bf16") for x in (q, k, v)))
+    shifts = [(8, 8), (0, 8)]
+    ref = []
+    for (qg, kg, vg), sh in zip(ins, shifts):
+        mem = S.pool_kv(kg, vg, grid, pool)
+        ref.append(S.window_attn(qg, kg, vg, grid, window, sh, mem=mem))
+    _sync()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(r) for r in ref]
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        _sync()
+        for st, (qg, kg, vg), sh, o in zip(streams, ins, shifts, outs):
+            with torch.cuda.stream(st):
+                mem = S.pool_kv(kg, vg, grid, pool)
+                S.window_attn(qg, kg, vg, grid, window, sh, mem=mem, out=o)
+        _sync()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"repetition {rep}"
+
+
 def test_binding_errors_before_launch():
     x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(S.BasaError):
