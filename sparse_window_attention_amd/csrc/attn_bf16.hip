@@ -1035,13 +1035,22 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
 #ifndef BASA_PERSISTENT_DMA
 #define BASA_PERSISTENT_DMA 1
 #endif
+// Per-device record of a kernel's raised LDS limit.
+struct DeviceFlags {
+  bool set[64] = {};
+};
+
+// Raises the kernel's dynamic LDS limit to 160 KB, once per device.
 template <typename K>
-int set_lds_limit(K kernel, bool& done) {
-  if (done) return BASA_OK;
+int set_lds_limit(K kernel, DeviceFlags& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BASA_ERR_HIP;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done.set[dev]) return BASA_OK;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
     return BASA_ERR_HIP;
-  done = true;  // benign race: the call is idempotent
+  if (cached) done.set[dev] = true;  // benign race: the call is idempotent
   return BASA_OK;
 }
 
@@ -1082,7 +1091,7 @@ int launch_persistent(const AttnParams& p0, hipStream_t stream) {
   if (nkt < kPersistentMinTiles || lds * BASA_PERSISTENT_WGS > 160 * 1024) return -1;
   AttnParams p = p0;
   if (int e = set_units(p, TL::kQT)) return e;
-  static bool attr = false;
+  static DeviceFlags attr;
   if (set_lds_limit(&attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>, attr)) return BASA_ERR_HIP;
   const int per_xcd = max(1, min(p.units_per_xcd, BASA_PERSISTENT_WGS * cu_count() / 8));
   hipLaunchKernelGGL((attn_bf16_persistent_kernel<D, FULL, NW, KT, DMA>),
@@ -1097,7 +1106,7 @@ int launch_unit(const AttnParams& p0, hipStream_t stream) {
   if (int e = set_units(p, TL::kQT)) return e;
   const size_t lds = TL::tileBytes + (FULL ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
-  static bool attr = false;
+  static DeviceFlags attr;
   if (set_lds_limit(&attn_bf16_kernel<D, FULL, NW, QB, KT>, attr)) return BASA_ERR_HIP;
   hipLaunchKernelGGL((attn_bf16_kernel<D, FULL, NW, QB, KT>), dim3((unsigned)(8 * p.units_per_xcd)),
                      dim3(TL::kThreads), lds, stream, p);

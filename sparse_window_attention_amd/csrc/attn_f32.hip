@@ -126,12 +126,14 @@ int launch(const AttnParams& p0, hipStream_t stream) {
   p.units = (int32_t)units;
   const size_t lds = 2 * kKT * D * sizeof(float) + (FULL ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
-  static bool attr_set = false;  // benign race: the call is idempotent
-  if (!attr_set) {
+  static bool attr_set[64] = {};  // per device; benign race: the call is idempotent
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BASA_ERR_HIP;
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_f32_kernel<D, FULL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return BASA_ERR_HIP;
-    attr_set = true;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
   hipLaunchKernelGGL((attn_f32_kernel<D, FULL>), dim3((unsigned)p.units), dim3(kThreads), lds,
                      stream, p);
