@@ -40,7 +40,10 @@
  *     Kernels run on the device current on the calling thread.  The library
  *     enqueues work and returns; it never synchronises the stream.
  *   - Ownership: the caller owns every buffer.  The library allocates no
- *     device memory and holds no state between calls (reentrant).
+ *     device memory and keeps no data between calls; its only process-wide
+ *     state is a per-device record of launch attributes already set (the
+ *     LDS limit, the compute-unit count).  Calls may run concurrently on
+ *     different streams.
  *   - Empty batches: batch or heads may be 0.  Such a call has nothing to
  *     do: it returns BASA_OK once head_dim, dtype and layout are valid,
  *     reads no pointer (they may be NULL, as an empty tensor's are) and
