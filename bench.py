@@ -119,22 +119,62 @@ def time_steps(S, wl, sets, steps, warmup, stream, with_mem=True):
         if ev is not None:
             ev[2].record(stream)
 
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
     for i in range(warmup):
         step(i)
+    host_s = (time.perf_counter() - h0) / max(warmup, 1)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # The host issues a step more slowly than the GPU runs it, so without a
+    # backlog the queue runs dry and a host stall between an event and the
+    # next launch would be counted as kernel time.  Queue GPU work lasting
+    # about twice the host's issue time for all steps ahead of them; the
+    # steps then run back to back from a full queue.
+    backlog_ok = _queue_backlog(2.0 * steps * max(host_s, 1e-4) + 0.005, stream)
     t0.record(stream)
     for i in range(steps):
         step(warmup + i, evs[i])
     t1.record(stream)
+    queued_ahead = backlog_ok and not t0.query()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
     pool = [e[0].elapsed_time(e[1]) for e in evs]
     attn = [e[1].elapsed_time(e[2]) for e in evs]
+    LAST_TIMING["queued_ahead"] = queued_ahead
     return total / steps, pool, attn
+
+
+LAST_TIMING = {}
+_BACKLOG = {}
+
+
+def _queue_backlog(seconds, stream):
+    """Enqueues plain bf16 matrix products lasting about `seconds` on the
+    stream (their results are discarded).  The product's time is measured
+    once.  Returns False if no product could be set up."""
+    import torch
+    try:
+        if "mm" not in _BACKLOG:
+            a = torch.randn((4096, 4096), device="cuda", dtype=torch.bfloat16)
+            c = torch.empty_like(a)
+            for _ in range(3):
+                torch.mm(a, a, out=c)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                torch.mm(a, a, out=c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            _BACKLOG["mm"] = (a, c, max(e0.elapsed_time(e1) / 10 * 1e-3, 1e-5))
+        a, c, t_mm = _BACKLOG["mm"]
+        for _ in range(min(int(math.ceil(seconds / t_mm)), 20000)):
+            torch.mm(a, a, out=c)
+        return True
+    except RuntimeError:
+        return False
 
 
 def time_steps_graph(S, wl, sets, steps, warmup, stream, with_mem=True):
@@ -182,10 +222,13 @@ def time_steps_graph(S, wl, sets, steps, warmup, stream, with_mem=True):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # the same start as the eager steps: behind a backlog, from a full queue
+    backlog_ok = _queue_backlog(0.005 + steps * 2e-4, stream)
     t0.record(stream)
     for i in range(steps):
         graphs[i % period].replay()
     t1.record(stream)
+    LAST_TIMING["graph_queued_ahead"] = backlog_ok and not t0.query()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps, ok
 
@@ -663,6 +706,9 @@ def measure_window(S, wl, args, stream, dev, with_dense=True):
         "step_launch": "hip graph per step" if graph_ok else "eager",
         "graph_output_equals_eager": graph_ok,
         "ms_per_step_eager_with_events": ms_eager,
+        "eager_steps_queued_ahead": LAST_TIMING.get("queued_ahead"),
+        "ms_per_step_graph": ms_graph,
+        "graph_steps_queued_ahead": LAST_TIMING.get("graph_queued_ahead"),
         "window_attn_ms": {"mean": attn_ms, "median": median(attn), "p10": pct(attn, 10),
                            "p90": pct(attn, 90)},
         "pool_kv_ms": {"mean": pool_ms, "median": median(pool)},
