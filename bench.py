@@ -468,55 +468,102 @@ def window_permutation(grid, window, shift, device):
     return perm.to(device), inv.to(device)
 
 
-def compose_attention(S, q, k, v, mem, grid, window, shift, perms=None):
-    """The composition a stock backend runs: materialised roll + partition of
-    Q, K, V; attention over the window-contiguous tensors (the library kernel
-    with the identity address map: a grid of nW rows of m tokens, one window
-    per row, the pooled memory shared); then unpartition + unroll of O."""
-    perm, inv = perms or window_permutation(grid, window, shift, q.device)
-    n = q.shape[2]
+def composition_index(B, H, grid, window, shift, device):
+    """Row indices of the stock-backend composition over a [B*H*n, D] view
+    of a BHND tensor: ``fwd`` takes it to window-batched order [B*nW, H, m,
+    D] (the grid rolled by -shift and cut into windows: row (b, j, h, r) is
+    token perm[j*m + r] of head (b, h)); ``inv`` takes a tensor in that
+    order back to [B, H, n, D] raster order (unpartition and roll by +shift)."""
+    import torch
+    perm, _ = window_permutation(grid, window, shift, "cpu")
+    n = perm.numel()
     m = int(math.prod(window))
-    qw, kw, vw = (x.index_select(2, perm) for x in (q, k, v))
-    ow = S.window_attn(qw, kw, vw, (n // m, m), (1, m), (0, 0), mem=mem)
-    return ow.index_select(2, inv)
+    nW = n // m
+    b = torch.arange(B).view(B, 1, 1, 1)
+    j = torch.arange(nW).view(1, nW, 1, 1)
+    h = torch.arange(H).view(1, 1, H, 1)
+    r = torch.arange(m).view(1, 1, 1, m)
+    fwd = ((b * H + h) * n + perm.view(nW, m)[j, r]).reshape(-1)
+    inv = torch.empty_like(fwd)
+    inv[fwd] = torch.arange(fwd.numel())
+    return fwd.to(device), inv.to(device)
+
+
+def compose_attention(S, q, k, v, mem, grid, window, shift, index=None, parts=None):
+    """The composition a stock backend runs (BASA forum summary, "Overview": no custom
+    operator, only existing dense attention kernels): materialised roll +
+    window partition of Q, K and V (one gather each, into [B*nW, H, m, D]);
+    each window's keys and values concatenated with the pooled memory (a
+    broadcast copy, [B*nW, H, m+G, D]); one unmodified dense attention call
+    over the B*nW window batches; then unpartition + unroll of O (a
+    gather).  ``parts``, if given, is a list that receives HIP events
+    bracketing the four phases."""
+    import torch
+    B, H, n, D = q.shape
+    m = int(math.prod(window))
+    nW = n // m
+    fwd, inv = index or composition_index(B, H, grid, window, shift, q.device)
+    ev = None
+    if parts is not None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record()
+    qw, kw, vw = (x.view(-1, D).index_select(0, fwd).view(B * nW, H, m, D) for x in (q, k, v))
+    if ev:
+        ev[1].record()
+    if mem is not None:
+        G = mem[0].shape[2]
+        kw, vw = (torch.cat([w.view(B, nW, H, m, D), x.unsqueeze(1).expand(B, nW, H, G, D)],
+                            dim=3).view(B * nW, H, m + G, D)
+                  for w, x in ((kw, mem[0]), (vw, mem[1])))
+    if ev:
+        ev[2].record()
+    ow = S.dense_attn(qw, kw, vw)
+    if ev:
+        ev[3].record()
+    out = ow.view(-1, D).index_select(0, inv).view(B, H, n, D)
+    if ev:
+        ev[4].record()
+        parts.append(ev)
+    return out
 
 
 def measure_composition(S, wl, sets, steps, stream):
-    """Times the composition baseline beside the fused kernel (events per
-    part); the memory broadcast a stock kernel would also need (every window's
-    copy of the pooled memory) is timed on its own."""
+    """Times the composition baseline (events per phase) on the rotated input
+    sets, beside the fused kernel it stands against."""
     import torch
-    B, H, n, D, G = wl.batch, wl.heads, wl.n_tokens, wl.head_dim, wl.mem_tokens
-    nW, m = wl.n_windows, wl.window_tokens
+    B, H = wl.batch, wl.heads
     shifts = [S.shift_for_block(i, wl.schedule, wl.window) for i in range(4)]
-    perms = [window_permutation(wl.grid, wl.window, sh, sets[0][0].device) for sh in shifts]
+    dev = sets[0][0].device
+    idx = [composition_index(B, H, wl.grid, wl.window, sh, dev) for sh in shifts]
     mems = [S.pool_kv(k, v, wl.grid, wl.pool) for (q, k, v) in sets]
-    parts = {"gather": [], "attention": [], "scatter": [], "broadcast": []}
+    evs = []
     for i in range(steps + 2):
         q, k, v = sets[i % len(sets)]
-        mem = mems[i % len(sets)]
-        perm, inv = perms[i % 4]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        ev[0].record(stream)
-        qw, kw, vw = (x.index_select(2, perm) for x in (q, k, v))
-        ev[1].record(stream)
-        ow = S.window_attn(qw, kw, vw, (nW, m), (1, m), (0, 0), mem=mem)
-        ev[2].record(stream)
-        ow.index_select(2, inv)
-        ev[3].record(stream)
-        mem[0].unsqueeze(2).expand(B, H, nW, G, D).contiguous()
-        mem[1].unsqueeze(2).expand(B, H, nW, G, D).contiguous()
-        ev[4].record(stream)
+        sink = [] if i >= 2 else None
+        compose_attention(S, q, k, v, mems[i % len(sets)], wl.grid, wl.window, shifts[i % 4],
+                          index=idx[i % 4], parts=sink)
         torch.cuda.synchronize()
-        if i >= 2:
-            for j, key in enumerate(parts):
-                parts[key].append(ev[j].elapsed_time(ev[j + 1]))
-    r = {key: sum(x) / len(x) for key, x in parts.items()}
-    r["total_without_broadcast"] = r["gather"] + r["attention"] + r["scatter"]
-    r["total_with_broadcast"] = r["total_without_broadcast"] + r["broadcast"]
-    r["note"] = ("materialised roll+partition (index_select), attention over the "
-                 "window-contiguous tensors, unpartition+unroll; broadcast = every window's "
-                 "copy of the pooled K/V memory that a stock dense kernel also needs")
+        if sink:
+            evs.append(sink[0])
+    names = ("roll_partition_gather", "memory_concat", "dense_attention", "unpartition_unroll")
+    r = {key: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / len(evs)
+         for j, key in enumerate(names)}
+    r["total"] = sum(r[key] for key in names)
+    m, G, D, n = wl.window_tokens, wl.mem_tokens, wl.head_dim, wl.n_tokens
+    tok = B * H * n * D * 2              # bytes of one bf16 [B, H, n, D] tensor
+    kvc = B * (n // m) * H * (m + G) * D * 2   # one [B*nW, H, m+G, D] key or value tensor
+    memb = B * H * G * D * 2
+    r["bytes_moved"] = {
+        "roll_partition_gather": 6 * tok,            # read and write Q, K, V
+        "memory_concat": 2 * (tok + memb + kvc),     # read K/V windows and memory, write K/V+mem
+        "dense_attention": 2 * tok + 2 * kvc,        # read Q, K, V, write O
+        "unpartition_unroll": 2 * tok,               # read and write O
+    }
+    r["bytes_moved_total"] = sum(r["bytes_moved"].values())
+    r["note"] = ("stock-backend composition: materialised roll+partition (one gather per "
+                 "tensor into [B*nW, H, m, D]), memory concatenated to every window's K/V "
+                 "([B*nW, H, m+G, D]), the library's dense kernel (basa_dense_attn) over the "
+                 "window batches, then unpartition+unroll (a gather); HIP events per phase")
     return r
 
 
@@ -827,10 +874,11 @@ def main():
     comp = measure_composition(S, head, comp_sets, max(10, args.steps // 2), stream)
     del comp_sets
     comp["fused_attention_ms"] = res["window_attn_ms"]["mean"]
-    comp["composition_over_fused"] = comp["total_with_broadcast"] / res["window_attn_ms"]["mean"]
-    print(f"[bench] composition baseline: gather {comp['gather']*1e3:.1f} + attention "
-          f"{comp['attention']*1e3:.1f} + scatter {comp['scatter']*1e3:.1f} + broadcast "
-          f"{comp['broadcast']*1e3:.1f} us", file=sys.stderr, flush=True)
+    comp["composition_over_fused"] = comp["total"] / res["window_attn_ms"]["mean"]
+    print(f"[bench] composition baseline: gather {comp['roll_partition_gather']*1e3:.1f} + "
+          f"memory concat {comp['memory_concat']*1e3:.1f} + dense "
+          f"{comp['dense_attention']*1e3:.1f} + unpartition "
+          f"{comp['unpartition_unroll']*1e3:.1f} us", file=sys.stderr, flush=True)
     bwd_sets = make_sets(head, 2, dev)
     bwd = measure_backward(S, head, bwd_sets, max(8, args.steps // 4), stream)
     del bwd_sets

@@ -295,6 +295,38 @@ int basa_full_attn(const void* q, const void* k, const void* v, void* out,
                    int32_t head_dim, float scale, int32_t dtype, int32_t layout,
                    void* stream);
 
+/*
+ * Dense attention with n_q queries and n_kv keys per (batch, head):
+ * out = softmax(scale * q k^T) v, with no window, shift or memory.  This is
+ * the unmodified dense kernel a stock backend provides [BASA-1, "Overview"
+ * and "The BASA Method": the method needs no custom operator and runs on
+ * existing dense attention backends once the roll and the window partition
+ * are materialised]; the composition baseline calls it over B*nW "batches"
+ * of [window keys; memory keys].  basa_full_attn is the case n_q = n_kv.
+ *   q, out   device, B x H x n_q x D in `layout`
+ *   k, v     device, B x H x n_kv x D in the same layout
+ *   n_q, n_kv >= 1; other arguments as basa_full_attn
+ * Errors: INVALID_ARG (NULL, sizes, alignment, out overlapping an input),
+ * UNSUPPORTED (dtype, head_dim, offsets beyond 32 bits), HIP (launch).
+ */
+int basa_dense_attn(const void* q, const void* k, const void* v, void* out,
+                    int32_t batch, int32_t heads, int64_t n_q, int64_t n_kv,
+                    int32_t head_dim, float scale, int32_t dtype, int32_t layout,
+                    void* stream);
+
+/*
+ * The shared central region of Hilbert-order tiles [HilbertA, abstract: a
+ * small central region that every tile also attends to]: raster indices
+ * y*grid_x + x of the size_y x size_x block of a grid_y x grid_x grid whose
+ * first row and column are (grid - size) / 2 (rounded down), in raster order
+ * (host).  The result is the idx argument of basa_gather_kv.
+ *   idx_out  host int32 [size_y * size_x], written
+ * Errors: INVALID_ARG for NULL, a size outside [1, grid] on either axis, or
+ * a grid of more than 2^31 - 1 tokens.
+ */
+int basa_center_region(int32_t grid_y, int32_t grid_x, int32_t size_y, int32_t size_x,
+                       int32_t* idx_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ __all__ = [
     "SCHED_NONE", "SCHED_ALTERNATE", "SCHED_FOUR_PHASE", "BasaError", "lib",
     "library_path", "version", "mem_tokens", "shift_for_block", "pool_kv",
     "window_attn", "window_attn_fwd", "window_attn_bwd", "bwd_workspace_bytes", "full_attn",
-    "hilbert_order", "center_region_tokens", "gather_kv", "curve_attn",
+    "dense_attn", "hilbert_order", "center_region_tokens", "gather_kv", "curve_attn",
 ]
 
 BASA_OK, BASA_ERR_INVALID_ARG, BASA_ERR_UNSUPPORTED, BASA_ERR_HIP = 0, 1, 2, 3
@@ -66,6 +66,9 @@ def _load() -> ctypes.CDLL:
                                             i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
         "basa_full_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i64, i32, f32, i32,
                                           i32, vp]),
+        "basa_dense_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i64, i64, i32, f32, i32,
+                                           i32, vp]),
+        "basa_center_region": (ctypes.c_int, [i32, i32, i32, i32, pi32]),
         "basa_window_attn_fwd": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32,
                                                 i32, pi32, pi32, pi32, f32, f32, i32, i32, vp]),
         "basa_window_attn_bwd_workspace": (i64, [i32, i32, i32, i32, pi32, pi32]),
@@ -94,6 +97,19 @@ def _arr(vals: Sequence[int]):
     return (ctypes.c_int32 * len(vals))(*vals)
 
 
+def _ndim(grid: Sequence[int], **parts) -> int:
+    """len(grid) after checking that it is 2 or 3 and that every other
+    geometry argument (window, shift, pool; None = absent) has as many
+    entries: the C side reads ndim entries from each array."""
+    nd = len(grid)
+    if nd not in (2, 3):
+        raise ValueError(f"grid must have 2 or 3 entries (got {nd})")
+    for name, val in parts.items():
+        if val is not None and len(val) != nd:
+            raise ValueError(f"{name} has {len(val)} entries; the grid has {nd}")
+    return nd
+
+
 def _check(status: int) -> None:
     if status != BASA_OK:
         raise BasaError(status, f"{lib.basa_status_string(status).decode()}: "
@@ -105,7 +121,7 @@ def version() -> int:
 
 
 def mem_tokens(grid: Sequence[int], pool: Sequence[int]) -> int:
-    g = lib.basa_mem_tokens(len(grid), _arr(grid), _arr(pool))
+    g = lib.basa_mem_tokens(_ndim(grid, pool=pool), _arr(grid), _arr(pool))
     if g < 0:
         raise BasaError(BASA_ERR_INVALID_ARG, lib.basa_last_error().decode())
     return int(g)
@@ -166,6 +182,7 @@ def pool_kv(k, v, grid: Sequence[int], pool: Sequence[int], layout: str = "bhnd"
             out: Optional[tuple] = None):
     """Mean-pooled memory (k_mem, v_mem), each [B, H, G, D]."""
     torch = _torch()
+    nd = _ndim(grid, pool=pool)
     _check_tensors(k, v)
     B, H, n, D, lay = _layout_dims(k, layout)
     if tuple(v.shape) != tuple(k.shape):
@@ -182,7 +199,7 @@ def pool_kv(k, v, grid: Sequence[int], pool: Sequence[int], layout: str = "bhnd"
     if n != math.prod(grid):
         raise ValueError("token count does not match the grid")
     _check(lib.basa_pool_kv(k.data_ptr(), v.data_ptr(), km.data_ptr(), vm.data_ptr(), B, H, D,
-                            len(grid), _arr(grid), _arr(pool), _dtype_code(k), lay, _stream(k)))
+                            nd, _arr(grid), _arr(pool), _dtype_code(k), lay, _stream(k)))
     return km, vm
 
 
@@ -191,6 +208,7 @@ def window_attn(q, k, v, grid: Sequence[int], window: Sequence[int], shift: Sequ
                 mem_bias: float = 0.0, out=None, layout: str = "bhnd"):
     """Shifted local window attention with optional pooled memory (k_mem, v_mem)."""
     torch = _torch()
+    nd = _ndim(grid, window=window, shift=shift)
     _check_tensors(q, k, v)
     B, H, n, D, lay = _layout_dims(q, layout)
     if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
@@ -217,7 +235,7 @@ def window_attn(q, k, v, grid: Sequence[int], window: Sequence[int], shift: Sequ
     if scale is not None and not scale > 0:
         raise ValueError("scale must be positive")
     _check(lib.basa_window_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, G,
-                                out.data_ptr(), B, H, D, len(grid), _arr(grid), _arr(window),
+                                out.data_ptr(), B, H, D, nd, _arr(grid), _arr(window),
                                 _arr(shift), s, float(mem_bias), _dtype_code(q), lay,
                                 _stream(q)))
     return out
@@ -240,6 +258,7 @@ def window_attn_fwd(q, k, v, grid: Sequence[int], window: Sequence[int], shift: 
     """window_attn that also returns the per-query log-sum-exp (fp32 [B, H, n])
     the backward needs: returns (out, lse)."""
     torch = _torch()
+    nd = _ndim(grid, window=window, shift=shift)
     _check_tensors(q, k, v)
     B, H, n, D, lay = _layout_dims(q, layout)
     if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
@@ -257,7 +276,7 @@ def window_attn_fwd(q, k, v, grid: Sequence[int], window: Sequence[int], shift: 
     if scale is not None and not scale > 0:
         raise ValueError("scale must be positive")
     _check(lib.basa_window_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, G,
-                                    out.data_ptr(), lse.data_ptr(), B, H, D, len(grid),
+                                    out.data_ptr(), lse.data_ptr(), B, H, D, nd,
                                     _arr(grid), _arr(window), _arr(shift), s, float(mem_bias),
                                     _dtype_code(q), lay, _stream(q)))
     return out, lse
@@ -265,7 +284,8 @@ def window_attn_fwd(q, k, v, grid: Sequence[int], window: Sequence[int], shift: 
 
 def bwd_workspace_bytes(batch: int, heads: int, head_dim: int, grid: Sequence[int],
                         pool: Optional[Sequence[int]] = None) -> int:
-    b = lib.basa_window_attn_bwd_workspace(int(batch), int(heads), int(head_dim), len(grid),
+    b = lib.basa_window_attn_bwd_workspace(int(batch), int(heads), int(head_dim),
+                                           _ndim(grid, pool=pool),
                                            _arr(grid), None if pool is None else _arr(pool))
     if b < 0:
         raise BasaError(BASA_ERR_INVALID_ARG, "invalid shape for the backward workspace")
@@ -280,6 +300,7 @@ def window_attn_bwd(q, k, v, out, dout, lse, grid: Sequence[int], window: Sequen
     """Gradients (dq, dk, dv) of window_attn; with memory, ``mem`` must be
     pool_kv(k, v, grid, pool) and its gradient is folded into dk and dv."""
     torch = _torch()
+    nd = _ndim(grid, window=window, shift=shift, pool=pool)
     _check_tensors(q, k, v, out, dout)
     B, H, n, D, lay = _layout_dims(q, layout)
     for t in (k, v, out, dout):
@@ -306,7 +327,7 @@ def window_attn_bwd(q, k, v, out, dout, lse, grid: Sequence[int], window: Sequen
     _check(lib.basa_window_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, out.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), B, H, D, len(grid), _arr(grid),
+        workspace.numel() * workspace.element_size(), B, H, D, nd, _arr(grid),
         _arr(window), _arr(shift), None if pool is None else _arr(pool), s, float(mem_bias),
         _dtype_code(q), lay, _stream(q)))
     return dq, dk, dv
@@ -342,6 +363,29 @@ def full_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "b
     return out
 
 
+def dense_attn(q, k, v, scale: Optional[float] = None, out=None, layout: str = "bhnd"):
+    """Dense softmax(scale q k^T) v with n_q queries and n_kv keys per (batch,
+    head): q [B, H, n_q, D], k and v [B, H, n_kv, D] (or the BNHD forms)."""
+    torch = _torch()
+    _check_tensors(q, k, v)
+    B, H, nq, D, lay = _layout_dims(q, layout)
+    Bk, Hk, nkv, Dk, _ = _layout_dims(k, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must share q's batch, heads and head dim, and one shape")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(q, out)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out shape differs from q")
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_dense_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H,
+                               nq, nkv, D, s, _dtype_code(q), lay, _stream(q)))
+    return out
+
+
 # ------------------------------------------------------- Hilbert-order tiles
 def hilbert_order(side: int):
     """Raster token index of every position of the Hilbert curve over a
@@ -354,13 +398,14 @@ def hilbert_order(side: int):
 
 def center_region_tokens(grid: Sequence[int], size: Sequence[int]):
     """Raster indices of the size[0] x size[1] block at the centre of a 2-D
-    grid (rows and columns starting at (grid - size) // 2), host numpy int32."""
+    grid (basa_center_region), host numpy int32."""
     import numpy as np
-    Hg, Wg = (int(x) for x in grid)
-    ch, cw = (int(x) for x in size)
-    y0, x0 = (Hg - ch) // 2, (Wg - cw) // 2
-    ys, xs = np.meshgrid(np.arange(y0, y0 + ch), np.arange(x0, x0 + cw), indexing="ij")
-    return (ys * Wg + xs).reshape(-1).astype(np.int32)
+    if len(grid) != 2 or len(size) != 2:
+        raise ValueError("grid and size must have 2 entries")
+    out = np.empty(int(size[0]) * int(size[1]), dtype=np.int32)
+    _check(lib.basa_center_region(int(grid[0]), int(grid[1]), int(size[0]), int(size[1]),
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return out
 
 
 def gather_kv(k, v, idx, layout: str = "bhnd", out: Optional[tuple] = None):

@@ -62,6 +62,11 @@ constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel 
 #ifndef BASA_PERSISTENT_WGS
 #define BASA_PERSISTENT_WGS 1
 #endif
+// Persistent kernel: spread the tiles of window keys among the tiles of
+// memory keys (1) or take the key tiles in key order (0).
+#ifndef BASA_TILE_INTERLEAVE
+#define BASA_TILE_INTERLEAVE 0
+#endif
 // Persistent kernel: stage the next unit's Q rows in LDS (1) or load them
 // into registers at the unit boundary (0).
 #ifndef BASA_PERSISTENT_QSTAGE
@@ -92,10 +97,12 @@ struct Tiles {
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-// One work unit: element offset of its (batch, head) slice in Q/K/V/O, its
-// (batch, head) index, window and query tile.
+// One work unit: element offset of its (batch, head) slice in Q/O (and, for
+// window attention, K/V), the same in K/V for dense attention, its (batch,
+// head) index, window and query tile.
 struct Unit {
   int64_t base;
+  int64_t kvbase;
   int bh;
   int win;
   int qt;
@@ -109,6 +116,7 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int unit) {
   u.bh = rest / p.nW;
   const int b = u.bh / p.heads, h = u.bh - b * p.heads;
   u.base = (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
+  u.kvbase = (int64_t)b * p.kv_stride_b + (int64_t)h * p.kv_stride_h;
   return u;
 }
 
@@ -145,7 +153,7 @@ struct Core {
     l32 = lane & 31;
     hf = lane >> 5;
     m = p.m;
-    L = m + p.G;
+    L = FULL ? p.n_kv : m + p.G;
     stb = (uint32_t)p.stride_tok * 2u;
     c1 = p.c1;
     bias = p.mem_bias_raw;
@@ -186,6 +194,8 @@ struct Core {
   __device__ __forceinline__ uint32_t tok(const uint32_t* t, int r) const {
     return FULL ? (uint32_t)r * stb : t[r];
   }
+  // element offset of the unit's (batch, head) slice of K and V
+  __device__ __forceinline__ int64_t kvb(const Unit& u) const { return FULL ? u.kvbase : u.base; }
 
   // ---- tile loader (global -> registers -> LDS).  Keys past the end are
   // clamped to the last key: those rows load valid data that the score mask
@@ -194,7 +204,7 @@ struct Core {
   __device__ __forceinline__ const char* row_ptr(const Unit& u, const uint32_t* t, int key,
                                                   bool isv) const {
     key = min(key, L - 1);
-    const char* g = reinterpret_cast<const char*>((isv ? p.v : p.k) + u.base);
+    const char* g = reinterpret_cast<const char*>((isv ? p.v : p.k) + kvb(u));
     if constexpr (FULL) return g + (uint32_t)key * stb;
     const char* gm = reinterpret_cast<const char*>((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
     const bool inwin = key < m;
@@ -212,13 +222,13 @@ struct Core {
     const int k0 = tile * kKT;
     const uint32_t cb = (uint32_t)chunk * 16u;
     if constexpr (FULL) {
-      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + kvb(u));
 #pragma unroll
       for (int i = 0; i < N; ++i)
         dst[i] = buf_load16(rs, (uint32_t)min(k0 + r0 + i * rstep, L - 1) * stb + cb, 0);
     } else {
       if (k0 + kKT <= m) {
-        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+        const Rsrc rs = make_rsrc((isv ? p.v : p.k) + kvb(u));
 #pragma unroll
         for (int i = 0; i < N; ++i) dst[i] = buf_load16(rs, t[k0 + r0 + i * rstep] + cb, 0);
         return;
@@ -331,13 +341,13 @@ struct Core {
       return (__attribute__((address_space(3))) void*)(buf + (wv * kDmaIpw + i) * 1024);
     };
     if constexpr (FULL) {
-      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + kvb(u));
 #pragma unroll
       for (int i = 0; i < kDmaIpw; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16,
                                                  (uint32_t)min(k0 + r[i], L - 1) * stb + cb[i], 0, 0, 0);
     } else if (k0 + kKT <= m) {
-      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + u.base);
+      const Rsrc rs = make_rsrc((isv ? p.v : p.k) + kvb(u));
 #pragma unroll
       for (int i = 0; i < kDmaIpw; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16, off[i] + cb[i], 0, 0, 0);
@@ -792,10 +802,34 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     if (c.L % kKT) tm = min(tm, c.nkt - 1);
     c.tmask = min(tm, c.nkt);
   }
+  // Order of the key tiles.  Position t of the loop processes key tile
+  // kt_of(t).  Before the first masked position (t1), the tiles of window
+  // keys (gathered from HBM) are spread evenly among the other tiles (memory
+  // keys, served from L2), so that every unit -- and with all compute units
+  // walking their units in step, the whole chip -- keeps reading HBM while
+  // it works through the memory keys instead of alternating a phase bound by
+  // HBM with one bound by the matrix cores.  The softmax does not depend on
+  // the order of its keys.  Of the first c positions, ceil(c * nw / t1) hold
+  // window tiles (nw of the t1); the division is a multiply by a rounded-up
+  // reciprocal, exact while t1 * t1 * (nw + 1) < 2^32 (t1 <= 1024, nw <= 64).
+  const int t1 = min(nkt, c.tmask);  // iterations t < t1 - 1 need no mask on S(t+1)
+  const int nw = (FULL || !BASA_TILE_INTERLEAVE || t1 > 1024) ? t1 : min(c.m / kKT, t1);
+  const uint32_t rcp =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu / (uint32_t)max(t1, 1) + 1u));
+  auto kt_of = [&](int pos) __attribute__((always_inline)) {
+    if (FULL || nw >= t1 || nw == 0 || pos >= t1) return pos;
+    const int c0 = (int)__umulhi((uint32_t)(pos * nw + t1 - 1), rcp);
+    const int c1n = (int)__umulhi((uint32_t)((pos + 1) * nw + t1 - 1), rcp);
+    return __builtin_amdgcn_readfirstlane(c1n > c0 ? c0 : nw + pos - c0);
+  };
+  // memory-key logit bias of position t taken as one offset (memory-only
+  // tiles before the masked ones)
   auto bias_of = [&](int t) __attribute__((always_inline)) {
     if constexpr (FULL) return 0.0f;  // no memory keys
-    else return (t < c.tmask && t * kKT >= c.m) ? c.bias : 0.0f;
+    else return (t < c.tmask && kt_of(t) * kKT >= c.m) ? c.bias : 0.0f;
   };
+  // key tiles of positions 0 and 1 (the same for every unit)
+  const int kt0 = kt_of(0), kt1 = kt_of(1);
   unsigned char* tables = smem + PL::tileBytes;
   // DMA tile buffers: K buffer b at b * kTileB, V buffer b at (2 + b) * kTileB
   auto dK = [&](int b) __attribute__((always_inline)) { return smem + b * C::kTileB; };
@@ -863,15 +897,15 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
   }
   load_q_of(uc, tab_of(0));
   if constexpr (DMA) {
-    get_k(uc, tab_of(0), 0);
-    get_v(uc, tab_of(0), 0);
-    get_k(uc, tab_of(0), 1);
+    c.dma_tile(dK(0), uc, tab_of(0), kt0, false);
+    c.dma_tile(dV(0), uc, tab_of(0), kt0, true);
+    c.dma_tile(dK(1), uc, tab_of(0), kt1, false);
     wait_vmem();
   } else {
     u32x4 k1[TL::KPASS];
-    c.load_k(uc, tab_of(0), 0);
-    c.load_v(uc, tab_of(0), 0);
-    c.load_k_to(k1, uc, tab_of(0), 1);
+    c.load_k(uc, tab_of(0), kt0);
+    c.load_v(uc, tab_of(0), kt0);
+    c.load_k_to(k1, uc, tab_of(0), kt1);
     c.store_k(0);
     c.store_v(0);
     c.store_k_from(k1, 1);
@@ -883,7 +917,6 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) dst[0][kb] = src[0][kb];
   };
-  const int t1 = min(nkt, c.tmask);  // iterations t < t1 - 1 need no mask on S(t+1)
   const int qstep = nkt - 2;         // staging load i of the next unit's Q goes out in
                                      // iteration i mod qstep (never in the last one)
 
@@ -903,8 +936,8 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       c.update_max(mx);
     }
     if constexpr (!DMA) {
-      c.load_v(uc, tab, 1);
-      c.load_k(uc, tab, 2);
+      c.load_v(uc, tab, kt1);
+      c.load_k(uc, tab, kt_of(2));
     }
     // Every wave is done with K(0) (and with the previous unit's output
     // rows, read through its table) before iteration 0 refills the buffer
@@ -912,7 +945,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     // loads into LDS go out only after this barrier: until then other waves
     // may still read the buffers (the previous unit's last V tile).
     lds_barrier();
-    if constexpr (DMA) c.dma_pair(true, dV(1), uc, tab, 1, true, dK(0), uc, tab, 2);
+    if constexpr (DMA) c.dma_pair(true, dV(1), uc, tab, kt1, true, dK(0), uc, tab, kt_of(2));
     if (!FULL && j >= 1 && has_next) c.build_table(tab_of(j + 1), un.win);
 
     // Iteration t: as in the unit kernel; the loads past the unit's last tile
@@ -943,18 +976,18 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
         const Unit u_v = cv ? uc : un;  // by value: the choice stays in registers
         const Unit u_k = ck ? uc : un;
         if (do_v || do_k)
-          c.dma_pair(do_v, dV(jv & 1), u_v, cv ? tab : tabn, jv, do_k, dK(jk & 1), u_k,
-                     ck ? tab : tabn, jk);
+          c.dma_pair(do_v, dV(jv & 1), u_v, cv ? tab : tabn, kt_of(jv), do_k, dK(jk & 1), u_k,
+                     ck ? tab : tabn, kt_of(jk));
       } else {
         if (do_v) {
           const bool cur = tv < nkt;
           const Unit u = cur ? uc : un;  // by value: the choice stays in registers
-          get_v(u, cur ? tab : tabn, cur ? tv : 0);
+          get_v(u, cur ? tab : tabn, cur ? kt_of(tv) : kt0);
         }
         if (do_k) {
           const bool cur = tk < nkt;
           const Unit u = cur ? uc : un;
-          get_k(u, cur ? tab : tabn, cur ? tk : tk - nkt);
+          get_k(u, cur ? tab : tabn, kt_of(cur ? tk : tk - nkt));
         }
       }
       if (has_next && t < qstep)
@@ -982,7 +1015,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       ++t;
       copy(sA, sB);
     }
-    {
+    if (t < c.nkt) {  // the tile padding an odd tile count holds no key
       Probs pb;
       c.make_p(sA, pb, bias_of(t) * c.c1);
       if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
@@ -1086,7 +1119,7 @@ int launch_persistent(const AttnParams& p0, hipStream_t stream) {
   constexpr bool DMA = BASA_PERSISTENT_DMA != 0;
   using TL = Tiles<D, NW, 1, KT>;
   using SL = PersistLayout<D, FULL, NW, KT, DMA>;
-  const int nkt = (p0.m + p0.G + KT - 1) / KT;
+  const int nkt = ((FULL ? p0.n_kv : p0.m + p0.G) + KT - 1) / KT;
   const size_t lds = SL::bytes(p0.m);
   if (nkt < kPersistentMinTiles || lds * BASA_PERSISTENT_WGS > 160 * 1024) return -1;
   AttnParams p = p0;

@@ -32,15 +32,17 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
   const int b = bh / p.heads, h = bh - b * p.heads;
   const int64_t base = (int64_t)b * p.stride_b + (int64_t)h * p.stride_h;
   const float* __restrict__ gq = reinterpret_cast<const float*>(p.q) + base;
-  const float* __restrict__ gk = reinterpret_cast<const float*>(p.k) + base;
-  const float* __restrict__ gv = reinterpret_cast<const float*>(p.v) + base;
+  const int64_t kvbase = FULL ? (int64_t)b * p.kv_stride_b + (int64_t)h * p.kv_stride_h : base;
+  const float* __restrict__ gk = reinterpret_cast<const float*>(p.k) + kvbase;
+  const float* __restrict__ gv = reinterpret_cast<const float*>(p.v) + kvbase;
   float* __restrict__ go = reinterpret_cast<float*>(p.out) + base;
   const float* __restrict__ gkm = reinterpret_cast<const float*>(p.kmem) + (int64_t)bh * p.G * D;
   const float* __restrict__ gvm = reinterpret_cast<const float*>(p.vmem) + (int64_t)bh * p.G * D;
 
   const int tid = threadIdx.x;
   const int m = p.m;
-  const int L = m + p.G;
+  const int L = FULL ? p.n_kv : m + p.G;
+  const int nwin = FULL ? L : m;  // keys read through the token map
   const int stok = p.stride_tok;
   if (!FULL) {
     for (int r = tid; r < m; r += kThreads) sOff[r] = slot_token(p, win, r) * stok;
@@ -68,7 +70,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
       const int r = i / C4, c = i % C4;
       const int key = k0 + r;
       f32x4 kx{0, 0, 0, 0}, vx{0, 0, 0, 0};
-      if (key < m) {
+      if (key < nwin) {
         const int32_t o = tokoff(key);
         kx = *reinterpret_cast<const f32x4*>(gk + o + 4 * c);
         vx = *reinterpret_cast<const f32x4*>(gv + o + 4 * c);
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = __builtin_fmaf(q[d], sK[j * D + d], dot);
       float x = dot * scale;
-      if (k0 + j >= m) x += p.mem_bias;
+      if (k0 + j >= nwin) x += p.mem_bias;
       s[j] = (j < nk) ? x : -INFINITY;
       mt = fmaxf(mt, s[j]);
     }

@@ -618,31 +618,36 @@ int basa_calib_mfma(float* sink, int32_t blocks, int32_t iters, void* stream) {
   }
 }
 
-int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
-                   int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
-                   int32_t layout, void* stream) {
+int basa_dense_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                    int32_t heads, int64_t n_q, int64_t n_kv, int32_t head_dim, float scale,
+                    int32_t dtype, int32_t layout, void* stream) {
   try {
     if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
     if (!q || !k || !v || !out) return fail(BASA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
-    if (n_tokens < 1) return fail(BASA_ERR_INVALID_ARG, "n_tokens must be >= 1");
+    if (n_q < 1 || n_kv < 1) return fail(BASA_ERR_INVALID_ARG, "n_q and n_kv must be >= 1");
     if (not_finite(scale)) return fail(BASA_ERR_INVALID_ARG, "scale must be finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
       return fail(BASA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-    int64_t sb, sh, stok;
-    strides(layout, heads, n_tokens, head_dim, &sb, &sh, &stok);
-    if (n_tokens * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "sequence too long for 32-bit token offsets");
+    int64_t sb, sh, stok, kb, kh, ktok;
+    strides(layout, heads, n_q, head_dim, &sb, &sh, &stok);
+    strides(layout, heads, n_kv, head_dim, &kb, &kh, &ktok);
+    if (n_q * stok >= INT32_MAX || n_kv * ktok >= INT32_MAX)
+      return fail(BASA_ERR_UNSUPPORTED, "sequence too long for 32-bit token offsets");
     const size_t es = dtype == BASA_BF16 ? 2 : 4;
-    const size_t tb = (size_t)batch * heads * n_tokens * head_dim * es;
-    if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+    const size_t qb = (size_t)batch * heads * n_q * head_dim * es;
+    const size_t kvb = (size_t)batch * heads * n_kv * head_dim * es;
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb))
       return fail(BASA_ERR_INVALID_ARG, "out overlaps an input");
     basa::AttnParams p{};
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
     p.kmem = nullptr; p.vmem = nullptr; p.out = (uint16_t*)out;
     p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
+    p.kv_stride_b = kb; p.kv_stride_h = kh;
     p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
-    p.m = (int32_t)n_tokens;
+    p.m = (int32_t)n_q;
+    p.n_kv = (int32_t)n_kv;
     p.G = 0;
     p.nW = 1;
     p.scale = resolve_scale(scale, head_dim);
@@ -650,10 +655,37 @@ int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32
     rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, true, (hipStream_t)stream)
                             : basa::launch_attn_f32(p, true, (hipStream_t)stream);
     if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
-    if (rc) return fail(rc, "full attention launch failed: %s", hipGetErrorString(hipGetLastError()));
+    if (rc) return fail(rc, "dense attention launch failed: %s", hipGetErrorString(hipGetLastError()));
     return ok();
   } catch (...) {
-    return fail(BASA_ERR_HIP, "unexpected exception in basa_full_attn");
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_dense_attn");
+  }
+}
+
+int basa_full_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                   int32_t heads, int64_t n_tokens, int32_t head_dim, float scale, int32_t dtype,
+                   int32_t layout, void* stream) {
+  return basa_dense_attn(q, k, v, out, batch, heads, n_tokens, n_tokens, head_dim, scale, dtype,
+                         layout, stream);
+}
+
+int basa_center_region(int32_t grid_y, int32_t grid_x, int32_t size_y, int32_t size_x,
+                       int32_t* idx_out) {
+  try {
+    if (!idx_out) return fail(BASA_ERR_INVALID_ARG, "idx_out must be non-NULL");
+    if (grid_y < 1 || grid_x < 1 || size_y < 1 || size_x < 1 || size_y > grid_y ||
+        size_x > grid_x)
+      return fail(BASA_ERR_INVALID_ARG, "need 1 <= size <= grid on both axes");
+    if ((int64_t)grid_y * grid_x > INT32_MAX)
+      return fail(BASA_ERR_INVALID_ARG, "grid too large for int32 token indices");
+    // the block's first row and column leave (grid - size) / 2 tokens before
+    // it (rounded down) and the rest after it
+    const int32_t y0 = (grid_y - size_y) / 2, x0 = (grid_x - size_x) / 2;
+    for (int32_t i = 0; i < size_y; ++i)
+      for (int32_t j = 0; j < size_x; ++j) idx_out[i * size_x + j] = (y0 + i) * grid_x + x0 + j;
+    return ok();
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_center_region");
   }
 }
 

@@ -40,6 +40,12 @@ struct AttnParams {
   const int32_t* order;   // optional device [n_tok]: a token order whose runs of m
                           // consecutive positions are the windows (replaces geo)
   int32_t slide;          // start of window 0 along `order`, in [0, n_tok)
+  // dense attention only: keys (and values) per (batch, head) and the strides
+  // of the K/V tensors between batches and heads (the token stride is
+  // stride_tok); for window attention the keys are the window's m tokens and
+  // the G memory rows, addressed with the strides of Q
+  int32_t n_kv;
+  int64_t kv_stride_b, kv_stride_h;
 };
 
 // Raster token of slot r of window `win`: under the shifted grid partition,

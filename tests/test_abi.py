@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(S.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +141,59 @@ def test_full_attn_validation():
         == S.BASA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 3 * SZ, 1, 1, 1 << 26, 128, -1.0, 1, 0,
              None) == S.BASA_ERR_UNSUPPORTED
+
+
+def test_dense_attn_validation():
+    f = S.lib.basa_dense_attn
+    q, k, v, o = FAKE, FAKE + SZ, FAKE + 2 * SZ, FAKE + 3 * SZ
+    for nq, nkv in ((0, 64), (64, 0), (-1, 64)):
+        assert f(q, k, v, o, 1, 2, nq, nkv, 128, -1.0, 1, 0, None) == S.BASA_ERR_INVALID_ARG
+    assert f(None, k, v, o, 1, 2, 64, 64, 128, -1.0, 1, 0, None) == S.BASA_ERR_INVALID_ARG
+    # out overlapping k, whose extent (n_kv rows) is larger than q's
+    assert f(q, k, v, k + 256 * 128 * 2, 1, 1, 16, 512, 128, -1.0, 1, 0, None) \
+        == S.BASA_ERR_INVALID_ARG
+    assert f(q, k, v, o, 1, 1, 64, 64, 96, -1.0, 1, 0, None) == S.BASA_ERR_UNSUPPORTED
+    assert f(q, k, v, o, 1, 1, 64, 1 << 26, 128, -1.0, 1, 0, None) == S.BASA_ERR_UNSUPPORTED
+    assert f(q, k, v, o, 1, 1, 64, 64, 128, float("nan"), 1, 0, None) == S.BASA_ERR_INVALID_ARG
+    assert f(None, None, None, None, 0, 3, 64, 32, 128, -1.0, 1, 0, None) == S.BASA_OK
+
+
+def test_center_region_validation():
+    out = (ctypes.c_int32 * 16)()
+    f = S.lib.basa_center_region
+    assert f(8, 8, 2, 2, out) == S.BASA_OK and list(out[:4]) == [27, 28, 35, 36]
+    for args in ((8, 8, 0, 2), (8, 8, 9, 2), (8, 8, 2, 9), (0, 8, 1, 1), (8, -1, 1, 1)):
+        assert f(*args, out) == S.BASA_ERR_INVALID_ARG, args
+    assert f(8, 8, 2, 2, None) == S.BASA_ERR_INVALID_ARG
+    assert f(1 << 16, 1 << 16, 1, 1, out) == S.BASA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        S.center_region_tokens((8, 8, 8), (2, 2))
+
+
+@pytest.mark.parametrize("call", ["mem_tokens", "pool_kv", "window_attn", "window_attn_fwd",
+                                  "window_attn_bwd", "bwd_workspace_bytes"])
+def test_binding_checks_geometry_lengths(call):
+    # the C side reads ndim = len(grid) entries of every geometry array: a
+    # shorter list would be read past its end, a longer one truncated, so the
+    # binding refuses both before any tensor is looked at
+    x = object()
+    grid3 = (21, 30, 52)
+    cases = {
+        "mem_tokens": [lambda: S.mem_tokens(grid3, (3, 5)),
+                       lambda: S.mem_tokens((8, 8), (4, 4, 1))],
+        "pool_kv": [lambda: S.pool_kv(x, x, grid3, (3, 5))],
+        "window_attn": [lambda: S.window_attn(x, x, x, grid3, (7, 10, 13), (3, 5)),
+                        lambda: S.window_attn(x, x, x, grid3, (7, 10), (3, 5, 6)),
+                        lambda: S.window_attn(x, x, x, (8, 8), (4, 4), (1, 1, 1)),
+                        lambda: S.window_attn(x, x, x, (2, 2, 2, 2), (1, 1, 1, 1), (0, 0, 0, 0))],
+        "window_attn_fwd": [lambda: S.window_attn_fwd(x, x, x, grid3, (7, 10, 13), (3, 5))],
+        "window_attn_bwd": [lambda: S.window_attn_bwd(x, x, x, x, x, x, grid3, (7, 10, 13),
+                                                      (3, 5, 6), pool=(3, 5))],
+        "bwd_workspace_bytes": [lambda: S.bwd_workspace_bytes(1, 1, 128, grid3, (3, 5))],
+    }
+    for fn in cases[call]:
+        with pytest.raises(ValueError):
+            fn()
 
 
 def test_binding_rejects_cpu_tensors():
@@ -296,6 +349,8 @@ def test_empty_batch_is_a_no_op():
                                   S.BASA_BF16, 0, None) == S.BASA_OK
         assert S.lib.basa_full_attn(None, None, None, None, B, H, 64, 128, -1.0, S.BASA_BF16, 0,
                                     None) == S.BASA_OK
+        assert S.lib.basa_dense_attn(None, None, None, None, B, H, 64, 96, 128, -1.0, S.BASA_BF16,
+                                     0, None) == S.BASA_OK
         assert S.lib.basa_gather_kv(None, None, None, 4, None, None, B, H, 128, 64, S.BASA_BF16, 0,
                                     None) == S.BASA_OK
         assert S.lib.basa_curve_attn(None, None, None, None, None, 0, None, B, H, 128, 64, None, 16,

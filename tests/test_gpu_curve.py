@@ -39,8 +39,9 @@ def test_hilbert_tiles(case, dtype):
     order = O.hilbert_order(side)
     mem = km = vm = None
     if region is not None:
+        # the library's region goes to the GPU; the oracle's is the reference
+        mem = S.gather_kv(kg, vg, _order(S.center_region_tokens((side, side), region)))
         reg = O.center_region((side, side), region)
-        mem = S.gather_kv(kg, vg, _order(reg))
         km, vm = k[:, :, reg], v[:, :, reg]
     out = S.curve_attn(qg, kg, vg, _order(S.hilbert_order(side)), tile, slide, mem=mem)
     torch.cuda.synchronize()
@@ -105,22 +106,28 @@ def test_gather_kv(dtype, layout):
     assert torch.equal(vo, vb.index_select(2, sel))
 
 
-def test_hilbert_flux_shape_sampled():
-    # 128 x 128 tokens, 24 heads, tile 256 with an 8 x 8 central region, the
-    # launch the benchmark times; sampled tiles of two heads against the oracle
-    side, tile, slide, B, H, D = 128, 256, 128, 1, 24, 128
+@pytest.mark.parametrize("slide", [0, 128])
+def test_hilbert_flux_shape(slide):
+    # 128 x 128 tokens, 24 heads, tile 256 with an 8 x 8 central region: the
+    # launch the benchmark times, with the library's own curve order and
+    # region on the GPU (the oracle's only as the reference).  The output
+    # starts NaN-filled; every element of every head must be written, and
+    # three whole heads match the oracle.
+    side, tile, B, H, D = 128, 256, 1, 24, 128
     n = side * side
-    log("hilbert 128x128 sampled")
+    log(f"hilbert 128x128 slide {slide}")
     g = torch.Generator(device="cuda")
-    g.manual_seed(21)
+    g.manual_seed(21 + slide)
     qg, kg, vg = (torch.randn((B, H, n, D), generator=g, device="cuda").to(torch.bfloat16)
                   for _ in range(3))
-    reg = O.center_region((side, side), (8, 8))
-    mem = S.gather_kv(kg, vg, _order(reg))
-    order = O.hilbert_order(side)
-    out = S.curve_attn(qg, kg, vg, _order(order), tile, slide, mem=mem)
+    mem = S.gather_kv(kg, vg, _order(S.center_region_tokens((side, side), (8, 8))))
+    out = torch.full_like(qg, float("nan"))
+    S.curve_attn(qg, kg, vg, _order(S.hilbert_order(side)), tile, slide, mem=mem, out=out)
     torch.cuda.synchronize()
-    for h in (0, 23):
+    assert not bool(torch.isnan(out).any()), "unwritten output elements"
+    reg = O.center_region((side, side), (8, 8))
+    order = O.hilbert_order(side)
+    for h in (0, 11, 23):
         q, k, v = (to_np(x[0:1, h:h + 1]) for x in (qg, kg, vg))
         ref = O.curve_attention(q, k, v, order, tile, slide, k[:, :, reg], v[:, :, reg])
         assert_close(to_np(out[0:1, h:h + 1]), ref, "bf16", f"flux hilbert head {h}")

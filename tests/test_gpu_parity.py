@@ -10,8 +10,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import (assert_close, bhnd_to_bnhd, log, make_full_inputs, random_qkv,
-                      sample_windows, to_gpu, to_np)
+from gpu_util import (assert_close, bhnd_to_bnhd, log, make_full_inputs, random_qkv, to_gpu,
+                      to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -166,34 +166,45 @@ def test_flux1024_full(block):
     assert_close(to_np(out), ref, "bf16", f"flux1024 block {block}")
 
 
-def _sampled_check(wl, shift, heads, windows, variant=0):
-    gpu, exact = make_full_inputs(wl, heads, variant)
+def _full_size_check(wl, shifts, heads_of, variant=0, with_mem=True):
+    """Window attention at the workload's full size, once per shift: the
+    output starts NaN-filled, every element of every head must be written,
+    and for each shift the whole output of the heads ``heads_of(shift)``
+    (seeded workload values) must match the oracle."""
+    all_heads = sorted({h for sh in shifts for h in heads_of(sh)})
+    gpu, exact = make_full_inputs(wl, all_heads, variant)
     qg, kg, vg = gpu
-    mem = None
-    if wl.pool is not None:
-        mem = S.pool_kv(kg, vg, wl.grid, wl.pool)
-    out = S.window_attn(qg, kg, vg, wl.grid, wl.window, shift, mem=mem)
-    _sync()
-    assert bool(torch.isfinite(out).all()), "non-finite output"
-    for h in heads:
-        q, k, v = exact[h]
-        km = vm = None
-        if wl.pool is not None:
-            km = O.pool_mean(k[None, None], wl.grid, wl.pool)[0, 0]
-            vm = O.pool_mean(v[None, None], wl.grid, wl.pool)[0, 0]
-        idx, ref = O.window_attention_head(q, k, v, wl.grid, wl.window, shift, km, vm,
-                                           windows=windows)
-        got = to_np(out[0, h][torch.from_numpy(idx.reshape(-1)).to(out.device)])
-        assert_close(got.reshape(ref.shape), ref, "bf16",
-                     f"{wl.name} head {h} shift {shift} windows {windows}")
+    use_mem = with_mem and wl.pool is not None
+    mem = S.pool_kv(kg, vg, wl.grid, wl.pool) if use_mem else None
+    mems = {}
+    for shift in shifts:
+        log(f"{wl.name} shift={shift} heads={heads_of(shift)}")
+        out = torch.full_like(qg, float("nan"))
+        S.window_attn(qg, kg, vg, wl.grid, wl.window, shift, mem=mem, out=out)
+        _sync()
+        assert not bool(torch.isnan(out).any()), f"unwritten output elements, shift {shift}"
+        for h in heads_of(shift):
+            q, k, v = (x[None, None] for x in exact[h])
+            if h not in mems:
+                mems[h] = ((O.pool_mean(k, wl.grid, wl.pool), O.pool_mean(v, wl.grid, wl.pool))
+                           if use_mem else (None, None))
+            km, vm = mems[h]
+            ref = O.window_attention(q, k, v, wl.grid, wl.window, shift, km, vm)[0, 0]
+            assert_close(to_np(out[0, h]), ref, "bf16", f"{wl.name} head {h} shift {shift}")
+
+
+def _schedule_shifts(wl, blocks):
+    return [S.shift_for_block(b, wl.schedule, wl.window) for b in blocks]
 
 
 @pytest.mark.parametrize("wl", [W.FLUX2048_W16, W.FLUX2048_W32], ids=lambda w: w.name)
-def test_flux2048_sampled(wl):
-    for block in range(4):
-        shift = S.shift_for_block(block, wl.schedule, wl.window)
-        log(f"{wl.name} block={block} shift={shift}")
-        _sampled_check(wl, shift, heads=[0, 13, 23], windows=sample_windows(wl.n_windows))
+def test_flux2048_full(wl):
+    # every head of the last phase of the four-phase schedule, and three
+    # heads of each of the other three phases, checked whole
+    shifts = _schedule_shifts(wl, range(4))
+    last = shifts[3]
+    _full_size_check(wl, shifts,
+                     lambda sh: list(range(wl.heads)) if sh == last else [0, 13, 23])
 
 
 NOMEM = [W.FLUX2048_W16.with_(name="flux2048_128x128_w16_nomem", pool=None),
@@ -201,29 +212,23 @@ NOMEM = [W.FLUX2048_W16.with_(name="flux2048_128x128_w16_nomem", pool=None),
 
 
 @pytest.mark.parametrize("wl", NOMEM, ids=lambda w: w.name)
-def test_flux2048_no_memory_sampled(wl):
+def test_flux2048_no_memory_full(wl):
     # 4 (w16) and 16 (w32) key tiles per unit and several units per
     # workgroup: the persistent kernel's shortest units, whose successor's
     # tile loads start in their second iteration
-    for block in (1, 3):
-        shift = S.shift_for_block(block, wl.schedule, wl.window)
-        log(f"{wl.name} block={block} shift={shift}")
-        _sampled_check(wl, shift, heads=[0, 23], windows=sample_windows(wl.n_windows))
+    _full_size_check(wl, _schedule_shifts(wl, (1, 3)), lambda sh: [0, 23])
 
 
 @pytest.mark.parametrize("wl", [W.WAN, W.WAN_G1638], ids=lambda w: w.name)
-def test_wan_sampled(wl):
-    for block in range(2):
-        shift = S.shift_for_block(block, wl.schedule, wl.window)
-        log(f"{wl.name} block={block} shift={shift}")
-        _sampled_check(wl, shift, heads=[0, 21, 39], windows=sample_windows(wl.n_windows))
+def test_wan_full(wl):
+    # both phases of the alternating schedule, three whole heads each
+    _full_size_check(wl, _schedule_shifts(wl, range(2)), lambda sh: [0, 21, 39])
 
 
-def test_ultra_sampled():
+def test_ultra_full():
+    # all 256 windows of two heads at the last phase of the schedule
     wl = W.ULTRA
-    shift = S.shift_for_block(3, wl.schedule, wl.window)
-    log(f"{wl.name} shift={shift}")
-    _sampled_check(wl, shift, heads=[5, 19], windows=sample_windows(wl.n_windows, 3))
+    _full_size_check(wl, _schedule_shifts(wl, (3,)), lambda sh: [5, 19])
 
 
 # ------------------------------------------------------ launch configurations
@@ -285,8 +290,10 @@ def test_full_attn_flux2048_sampled():
     heads = [5, 18]
     log(f"dense {wl.name} heads {heads}")
     (qg, kg, vg), exact = make_full_inputs(wl, heads)
-    out = S.full_attn(qg, kg, vg)
+    out = torch.full_like(qg, float("nan"))
+    S.full_attn(qg, kg, vg, out=out)
     _sync()
+    assert not bool(torch.isnan(out).any()), "unwritten output elements"
     rows = np.unique(np.linspace(0, wl.n_tokens - 1, 80).astype(np.int64))
     for h in heads:
         q, k, v = exact[h]
@@ -307,6 +314,42 @@ def test_full_attn(dtype, n, D):
     rows = np.unique(np.linspace(0, n - 1, min(n, 300)).astype(np.int64))
     ref = O.full_attention(q, k, v, rows=rows)
     assert_close(to_np(out)[:, :, rows], ref, dtype, f"full {dtype} n{n} D{D}")
+
+
+DENSE = [
+    # dtype, n_q, n_kv, D, layout: the persistent kernel (>= 4 key tiles) and
+    # the per-unit kernel, ragged query and key counts, more queries than
+    # keys, the window batches of the composition baseline (256 x 512)
+    ("bf16", 256, 512, 128, "bhnd"),
+    ("bf16", 910, 1456, 128, "bhnd"),
+    ("bf16", 100, 1000, 64, "bnhd"),
+    ("bf16", 1000, 64, 128, "bhnd"),
+    ("bf16", 3000, 200, 128, "bnhd"),
+    ("f32", 300, 77, 64, "bhnd"),
+    ("f32", 64, 520, 128, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DENSE)))
+def test_dense_attn_unequal_lengths(case):
+    dtype, nq, nkv, D, layout = DENSE[case]
+    B, H = 2, 3
+    log(f"dense {dtype} n_q={nq} n_kv={nkv} D={D} {layout}")
+    rng = np.random.default_rng(600 + case)
+    q = rng.standard_normal((B, H, nq, D), dtype=np.float32)
+    k = rng.standard_normal((B, H, nkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, nkv, D), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = (W.round_bf16(x) for x in (q, k, v))
+    conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)
+    qg, kg, vg = (to_gpu(conv(x), dtype) for x in (q, k, v))
+    out = torch.full_like(qg, float("nan"))
+    S.dense_attn(qg, kg, vg, out=out, layout=layout)
+    _sync()
+    got = to_np(out)
+    if layout == "bnhd":
+        got = got.transpose(0, 2, 1, 3)
+    assert_close(got, O.full_attention(q, k, v), dtype, f"dense {nq}x{nkv} {dtype}")
 
 
 def test_window_equal_grid_matches_full_kernel():

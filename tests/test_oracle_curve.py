@@ -1,6 +1,8 @@
 """Pins of the Hilbert-tile oracle (oracle/basa_curve.py) and the library's
 host-side Hilbert order."""
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -36,10 +38,53 @@ def test_library_hilbert_order_matches_oracle(side):
     assert np.array_equal(S.hilbert_order(side), O.hilbert_order(side))
 
 
-def test_library_center_region_matches_oracle():
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "center_region.json")
+
+
+def _golden_regions():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _check_region(idx, case):
+    idx = [int(x) for x in idx]
+    Hg, Wg = case["grid"]
+    ch, cw = case["size"]
+    assert len(idx) == ch * cw
+    assert divmod(idx[0], Wg) == tuple(case["first"])
+    if "tokens" in case:
+        assert idx == case["tokens"]
+    else:
+        assert idx[:cw] == case["first_row"] and idx[-1] == case["last"]
+
+
+@pytest.mark.parametrize("case", range(7))
+def test_oracle_center_region_hand_worked(case):
+    c = _golden_regions()[case]
+    _check_region(O.center_region(c["grid"], c["size"]), c)
+
+
+@pytest.mark.parametrize("case", range(7))
+def test_library_center_region_hand_worked(case):
     S = pytest.importorskip("sparse_window_attention_amd")
-    for grid, size in [((8, 8), (2, 2)), ((64, 64), (8, 8)), ((10, 12), (3, 4))]:
-        assert np.array_equal(S.center_region_tokens(grid, size), O.center_region(grid, size))
+    c = _golden_regions()[case]
+    _check_region(S.center_region_tokens(c["grid"], c["size"]), c)
+
+
+@pytest.mark.parametrize("grid,size", [((9, 9), (3, 3)), ((9, 10), (4, 3)), ((2, 7), (1, 6)),
+                                       ((16, 16), (16, 1)), ((33, 20), (8, 8))])
+def test_oracle_center_region_is_centred_block(grid, size):
+    # a whole size[0] x size[1] block of the grid in raster order, with as
+    # many rows (columns) before it as after it, or one fewer
+    idx = O.center_region(grid, size)
+    ys, xs = np.divmod(idx, grid[1])
+    rows, cols = sorted(set(ys.tolist())), sorted(set(xs.tolist()))
+    assert rows == list(range(rows[0], rows[0] + size[0]))
+    assert cols == list(range(cols[0], cols[0] + size[1]))
+    assert list(idx) == sorted(idx) and len(idx) == size[0] * size[1]
+    for before, n, s in ((rows[0], grid[0], size[0]), (cols[0], grid[1], size[1])):
+        after = n - s - before
+        assert after - before in (0, 1)
 
 
 @pytest.mark.parametrize("tile,slide,mem", [(16, 0, False), (16, 5, True), (64, 40, True),
