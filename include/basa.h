@@ -40,10 +40,12 @@
  *     Kernels run on the device current on the calling thread.  The library
  *     enqueues work and returns; it never synchronises the stream.
  *   - Ownership: the caller owns every buffer.  The library allocates no
- *     device memory and keeps no data between calls; its only process-wide
- *     state is a per-device record of launch attributes already set (the
- *     LDS limit, the compute-unit count).  Calls may run concurrently on
- *     different streams.
+ *     device memory and keeps no data between calls; its process-wide state
+ *     is a per-device record of launch attributes already set (the LDS
+ *     limit, the compute-unit count) and, for basa_window_attn_bwd_noalloc
+ *     only, one static scratch array per GPU (see there).  Calls may run
+ *     concurrently on different streams, except basa_window_attn_bwd_noalloc
+ *     calls on one GPU.
  *   - Empty batches: batch or heads may be 0.  Such a call has nothing to
  *     do: it returns BASA_OK once head_dim, dtype and layout are valid,
  *     reads no pointer (they may be NULL, as an empty tensor's are) and
@@ -76,6 +78,10 @@ enum { BASA_SCHED_NONE = 0, BASA_SCHED_ALTERNATE = 1, BASA_SCHED_FOUR_PHASE = 2 
 
 /* Largest window (tokens per window) basa_window_attn accepts. */
 #define BASA_MAX_WINDOW_TOKENS 4096
+
+/* Bytes of the per-GPU scratch array basa_window_attn_bwd_noalloc uses as its
+ * workspace (64 MiB). */
+#define BASA_BWD_SCRATCH_BYTES (64ll << 20)
 
 /* Library ABI version (major*100 + minor). */
 int32_t basa_version(void);
@@ -222,6 +228,32 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v,
                          const int32_t* shift, const int32_t* pool,
                          float scale, float mem_bias,
                          int32_t dtype, int32_t layout, void* stream);
+
+/*
+ * basa_window_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Arguments, results and errors as
+ * basa_window_attn_bwd.  The call allocates nothing: its workspace is a
+ * static device array of BASA_BWD_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on, from its first use there to the end of the process.
+ * To fit that array the memory-key gradients are summed over query chunks
+ * larger than the workspace form uses (1024 queries, doubled as needed), so
+ * those sums are grouped differently and dk, dv may differ from
+ * basa_window_attn_bwd's in the last bits.  A shape whose workspace does not
+ * fit even with one chunk per head returns BASA_ERR_UNSUPPORTED (nothing is
+ * launched); at 24 heads of 16384 tokens, D = 128, 256 memory tokens it
+ * needs 58 MB.  Every call on one GPU uses that GPU's one array and leaves
+ * its contents behind (no part of it needs to start at zero): calls that
+ * overlap in time on one GPU (other streams, other threads) race on it and
+ * give undefined results; serialise them.
+ */
+int basa_window_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* k_mem, const void* v_mem, const void* out,
+                                 const void* dout, const float* lse, void* dq, void* dk,
+                                 void* dv, int32_t batch, int32_t heads, int32_t head_dim,
+                                 int32_t ndim, const int32_t* grid, const int32_t* window,
+                                 const int32_t* shift, const int32_t* pool, float scale,
+                                 float mem_bias, int32_t dtype, int32_t layout, void* stream);
 
 /*
  * Token order along a Hilbert curve of a side x side grid [HilbertA,

@@ -18,7 +18,8 @@ __all__ = [
     "BASA_F32", "BASA_BF16", "BASA_LAYOUT_BHND", "BASA_LAYOUT_BNHD",
     "SCHED_NONE", "SCHED_ALTERNATE", "SCHED_FOUR_PHASE", "BasaError", "lib",
     "library_path", "version", "mem_tokens", "shift_for_block", "pool_kv",
-    "window_attn", "window_attn_fwd", "window_attn_bwd", "bwd_workspace_bytes", "full_attn",
+    "window_attn", "window_attn_fwd", "window_attn_bwd", "window_attn_bwd_noalloc",
+    "bwd_workspace_bytes", "full_attn",
     "dense_attn", "hilbert_order", "center_region_tokens", "gather_kv", "curve_attn",
 ]
 
@@ -81,6 +82,9 @@ def _load() -> ctypes.CDLL:
         "basa_window_attn_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 i64, i32, i32, i32, i32, pi32, pi32, pi32, pi32,
                                                 f32, f32, i32, i32, vp]),
+        "basa_window_attn_bwd_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                        vp, i32, i32, i32, i32, pi32, pi32, pi32,
+                                                        pi32, f32, f32, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -328,6 +332,46 @@ def window_attn_bwd(q, k, v, out, dout, lse, grid: Sequence[int], window: Sequen
         q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, out.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), B, H, D, nd, _arr(grid),
+        _arr(window), _arr(shift), None if pool is None else _arr(pool), s, float(mem_bias),
+        _dtype_code(q), lay, _stream(q)))
+    return dq, dk, dv
+
+
+def window_attn_bwd_noalloc(q, k, v, out, dout, lse, grid: Sequence[int],
+                            window: Sequence[int], shift: Sequence[int],
+                            mem: Optional[tuple] = None, pool: Optional[Sequence[int]] = None,
+                            scale: Optional[float] = None, mem_bias: float = 0.0,
+                            grads: Optional[tuple] = None, layout: str = "bhnd"):
+    """window_attn_bwd with the library's static per-GPU scratch array as the
+    workspace (basa_window_attn_bwd_noalloc): the library allocates nothing.
+    ``grads`` (dq, dk, dv) are the caller's outputs; pass them to keep the
+    call free of allocations on the torch side as well."""
+    torch = _torch()
+    nd = _ndim(grid, window=window, shift=shift, pool=pool)
+    _check_tensors(q, k, v, out, dout)
+    B, H, n, D, lay = _layout_dims(q, layout)
+    for t in (k, v, out, dout):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError("q, k, v, out, dout shapes differ")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on q's device")
+    if (mem is None) != (pool is None):
+        raise ValueError("mem and pool go together")
+    km_p, vm_p, _ = _mem_args(q, mem, B, H, D)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = grads
+    _check_tensors(q, dq, dk, dv)
+    for t in grads:
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError("gradient outputs must have q's shape")
+    s = -1.0 if scale is None else float(scale)
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive")
+    _check(lib.basa_window_attn_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), km_p, vm_p, out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, D, nd, _arr(grid),
         _arr(window), _arr(shift), None if pool is None else _arr(pool), s, float(mem_bias),
         _dtype_code(q), lay, _stream(q)))
     return dq, dk, dv

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "basa_internal.h"
 
 namespace {
@@ -117,6 +119,33 @@ void strides(int32_t layout, int32_t heads, int64_t n, int32_t D, int64_t* sb, i
 }
 
 float resolve_scale(float scale, int32_t D) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)D); }
+
+// Workspace of basa_window_attn_bwd_noalloc: one array per GPU, from the
+// library's first use on that GPU to the end of the process.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+__device__ __align__(256) unsigned char scratch[BASA_BWD_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_addr[64];
+
+// Device address of the current device's scratch array.
+int scratch_address(void** addr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BASA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(BASA_ERR_UNSUPPORTED, "device index %d beyond 63", dev);
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    // two threads may both get here on a device's first call: both store the
+    // same address
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || a == nullptr)
+      return fail(BASA_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *addr = a;
+  return BASA_OK;
+}
 
 }  // namespace
 
@@ -332,9 +361,10 @@ struct BwdWorkspace {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-BwdWorkspace bwd_workspace(int64_t bh, int64_t n, int64_t G, int32_t head_dim) {
+BwdWorkspace bwd_workspace(int64_t bh, int64_t n, int64_t G, int32_t head_dim,
+                           int64_t qchunk = kBwdQueryChunk) {
   BwdWorkspace w{};
-  const int64_t nqc = (n + kBwdQueryChunk - 1) / kBwdQueryChunk;
+  const int64_t nqc = (n + qchunk - 1) / qchunk;
   size_t off = 0;
   w.dvec = off; off += align256((size_t)bh * n * 4);
   const size_t part = G ? (size_t)bh * nqc * G * head_dim * 4 : 0;
@@ -369,16 +399,21 @@ int64_t basa_window_attn_bwd_workspace(int32_t batch, int32_t heads, int32_t hea
   }
 }
 
-int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void* k_mem,
+namespace {
+
+// The backward with a caller's workspace, or (use_scratch) with the static
+// scratch array, the memory-key query chunk then enlarged until the
+// workspace fits it.
+int window_attn_bwd_impl(const void* q, const void* k, const void* v, const void* k_mem,
                          const void* v_mem, const void* out, const void* dout, const float* lse,
                          void* dq, void* dk, void* dv, void* workspace, int64_t workspace_bytes,
-                         int32_t batch, int32_t heads, int32_t head_dim, int32_t ndim,
-                         const int32_t* grid, const int32_t* window, const int32_t* shift,
-                         const int32_t* pool, float scale, float mem_bias, int32_t dtype,
-                         int32_t layout, void* stream) {
-  try {
+                         bool use_scratch, int32_t batch, int32_t heads, int32_t head_dim,
+                         int32_t ndim, const int32_t* grid, const int32_t* window,
+                         const int32_t* shift, const int32_t* pool, float scale, float mem_bias,
+                         int32_t dtype, int32_t layout, void* stream) {
+  {
     if (const int e = empty_call(batch, heads, head_dim, dtype, layout); e >= 0) return e;
-    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || (!workspace && !use_scratch))
       return fail(BASA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
     int rc = check_common(batch, heads, head_dim, dtype, layout);
     if (rc) return rc;
@@ -409,10 +444,24 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
     int64_t sb, sh, stok;
     strides(layout, heads, n, head_dim, &sb, &sh, &stok);
     if (n * stok >= INT32_MAX) return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit token offsets");
-    const BwdWorkspace ws = bwd_workspace((int64_t)batch * heads, n, G, head_dim);
-    if (workspace_bytes < (int64_t)ws.total)
+    int64_t qchunk = kBwdQueryChunk;
+    BwdWorkspace ws = bwd_workspace((int64_t)batch * heads, n, G, head_dim, qchunk);
+    if (use_scratch) {
+      // fewer, longer query chunks: fewer memory-key partials to keep
+      while (ws.total > (size_t)BASA_BWD_SCRATCH_BYTES && qchunk < n) {
+        qchunk *= 2;
+        ws = bwd_workspace((int64_t)batch * heads, n, G, head_dim, qchunk);
+      }
+      if (ws.total > (size_t)BASA_BWD_SCRATCH_BYTES)
+        return fail(BASA_ERR_UNSUPPORTED,
+                    "the backward needs %lld bytes of workspace, more than the %lld-byte scratch "
+                    "array (use basa_window_attn_bwd with a workspace)",
+                    (long long)ws.total, (long long)BASA_BWD_SCRATCH_BYTES);
+      workspace_bytes = (int64_t)ws.total;
+    } else if (workspace_bytes < (int64_t)ws.total) {
       return fail(BASA_ERR_INVALID_ARG, "workspace of %lld bytes is smaller than the %lld needed",
                   (long long)workspace_bytes, (long long)ws.total);
+    }
     const size_t tb = (size_t)batch * heads * n * head_dim * 2;
     const size_t mb = (size_t)batch * heads * G * head_dim * 2;
     const size_t lb = (size_t)batch * heads * n * 4;
@@ -433,6 +482,7 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
     if (overlaps(workspace, ws.total, lse, lb) || overlaps(workspace, ws.total, k_mem, mb) ||
         overlaps(workspace, ws.total, v_mem, mb))
       return fail(BASA_ERR_INVALID_ARG, "the workspace overlaps an input");
+    if (use_scratch && (rc = scratch_address(&workspace))) return rc;
 
     basa::BwdParams p{};
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
@@ -446,8 +496,8 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
     p.stride_b = sb; p.stride_h = sh; p.stride_tok = (int32_t)stok;
     p.heads = heads; p.batch_heads = batch * heads; p.head_dim = head_dim;
     p.n = (int32_t)n; p.m = (int32_t)m; p.G = (int32_t)G; p.nW = (int32_t)(n / m);
-    p.qchunk = (int32_t)kBwdQueryChunk;
-    p.nqc = (int32_t)((n + kBwdQueryChunk - 1) / kBwdQueryChunk);
+    p.qchunk = (int32_t)qchunk;
+    p.nqc = (int32_t)((n + qchunk - 1) / qchunk);
     p.scale = resolve_scale(scale, head_dim);
     p.c1 = p.scale * basa::kLog2e;
     p.mem_bias_raw = G ? mem_bias / p.scale : 0.0f;
@@ -465,8 +515,40 @@ int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void
     if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "backward launch shape not supported");
     if (rc) return fail(rc, "backward launch failed: %s", hipGetErrorString(hipGetLastError()));
     return ok();
+  }
+}
+
+}  // namespace
+
+int basa_window_attn_bwd(const void* q, const void* k, const void* v, const void* k_mem,
+                         const void* v_mem, const void* out, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, void* workspace, int64_t workspace_bytes,
+                         int32_t batch, int32_t heads, int32_t head_dim, int32_t ndim,
+                         const int32_t* grid, const int32_t* window, const int32_t* shift,
+                         const int32_t* pool, float scale, float mem_bias, int32_t dtype,
+                         int32_t layout, void* stream) {
+  try {
+    return window_attn_bwd_impl(q, k, v, k_mem, v_mem, out, dout, lse, dq, dk, dv, workspace,
+                                workspace_bytes, false, batch, heads, head_dim, ndim, grid, window,
+                                shift, pool, scale, mem_bias, dtype, layout, stream);
   } catch (...) {
     return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn_bwd");
+  }
+}
+
+int basa_window_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* k_mem,
+                                 const void* v_mem, const void* out, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, int32_t batch,
+                                 int32_t heads, int32_t head_dim, int32_t ndim,
+                                 const int32_t* grid, const int32_t* window,
+                                 const int32_t* shift, const int32_t* pool, float scale,
+                                 float mem_bias, int32_t dtype, int32_t layout, void* stream) {
+  try {
+    return window_attn_bwd_impl(q, k, v, k_mem, v_mem, out, dout, lse, dq, dk, dv, nullptr, 0,
+                                true, batch, heads, head_dim, ndim, grid, window, shift, pool,
+                                scale, mem_bias, dtype, layout, stream);
+  } catch (...) {
+    return fail(BASA_ERR_HIP, "unexpected exception in basa_window_attn_bwd_noalloc");
   }
 }
 

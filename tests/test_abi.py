@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(S.library_path)
     for n in names:
         assert hasattr(lib, n), n
@@ -253,6 +253,44 @@ def _bwd(**kw):
 def test_backward_validation(kw, code):
     assert _bwd(**kw) == code
     assert len(S.lib.basa_last_error().decode()) > 5
+
+
+def _bwd_noalloc(space=SZ, **kw):
+    a = dict(q=FAKE, k=FAKE + space, v=FAKE + 2 * space, km=FAKE + 3 * space,
+             vm=FAKE + 4 * space, out=FAKE + 5 * space, dout=FAKE + 6 * space,
+             lse=FAKE + 7 * space, dq=FAKE + 8 * space, dk=FAKE + 9 * space,
+             dv=FAKE + 10 * space, B=1, H=2, D=128, grid=(8, 8), window=(4, 4), shift=(0, 0),
+             pool=(4, 4), scale=-1.0, bias=0.0, dtype=S.BASA_BF16, layout=S.BASA_LAYOUT_BHND)
+    a.update(kw)
+    arr = lambda x: None if x is None else (ctypes.c_int32 * len(x))(*x)
+    return S.lib.basa_window_attn_bwd_noalloc(
+        a["q"], a["k"], a["v"], a["km"], a["vm"], a["out"], a["dout"], a["lse"], a["dq"],
+        a["dk"], a["dv"], a["B"], a["H"], a["D"], len(a["grid"]), arr(a["grid"]),
+        arr(a["window"]), arr(a["shift"]), arr(a["pool"]), a["scale"], a["bias"], a["dtype"],
+        a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), S.BASA_ERR_INVALID_ARG),
+    (dict(pool=None), S.BASA_ERR_INVALID_ARG),
+    (dict(window=(3, 4)), S.BASA_ERR_INVALID_ARG),
+    (dict(dq=FAKE + 64), S.BASA_ERR_INVALID_ARG),
+    (dict(dtype=S.BASA_F32), S.BASA_ERR_UNSUPPORTED),
+])
+def test_noalloc_backward_validation(kw, code):
+    # argument errors are reported before the scratch array is looked up
+    assert _bwd_noalloc(**kw) == code
+
+
+def test_noalloc_backward_rejects_workspace_beyond_scratch():
+    # 24 heads of the 512 x 512 grid with 4096 memory tokens: even one query
+    # chunk per head needs 25 MB of row sums and 2 x 50 MB of memory sums,
+    # more than the scratch array; rejected before any HIP call
+    big = 1 << 34
+    rc = _bwd_noalloc(space=big, H=24, grid=(512, 512), window=(32, 32), pool=(8, 8))
+    assert rc == S.BASA_ERR_UNSUPPORTED
+    msg = S.lib.basa_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg
 
 
 def test_backward_workspace_size():
