@@ -62,6 +62,14 @@ constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel 
 #ifndef BASA_PERSISTENT_WGS
 #define BASA_PERSISTENT_WGS 1
 #endif
+// Persistent kernel with direct tile loads: K tile buffers (2 or 3).  With
+// three, the K tile of position t+4 is loaded during iteration t and waited
+// for only at the end of iteration t+2 (two iterations of load latency
+// hidden instead of one); V keeps two buffers.  Three measured 1-3% slower
+// than two (the tile loads are not late), so two is the default.
+#ifndef BASA_K_DEPTH
+#define BASA_K_DEPTH 2
+#endif
 // Persistent kernel: spread the tiles of window keys among the tiles of
 // memory keys (1) or take the key tiles in key order (0).
 #ifndef BASA_TILE_INTERLEAVE
@@ -516,6 +524,12 @@ struct Core {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = rowmax(s, qb);
   }
+  // the first tile's max right after reset(): with the running max at -inf
+  // the rescale of update_max would only multiply zeros, so it is skipped
+  __device__ __forceinline__ void start_max(const float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_used[qb] = mx[qb] * c1;
+  }
   // lagging max: rescale O only when the max has grown by more than the slack
   __device__ __forceinline__ void update_max(const float (&mx)[QB]) {
 #pragma unroll
@@ -666,7 +680,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / (NW * QB)) attn_bf16_kernel(AttnP
   c.compute_s(c.sK(0), sA);
   if (c.tmask == 0) c.mask_s(sA, 0);
   c.rowmax_all(sA, mx);
-  c.update_max(mx);
+  c.start_max(mx);
   __syncthreads();  // every wave is done with K(0) before iteration 0 refills its buffer
 
   // Iteration t: S(t+1) from K buffer (t+1)&1 while P(t) is formed; P(t) V(t)
@@ -737,6 +751,14 @@ __device__ __forceinline__ void lds_barrier() {
 // Waits until every vector memory operation of this wave has completed
 // (vmcnt = 0; expcnt and lgkmcnt left at their maximum).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most N of this wave's vector memory operations are
+// outstanding (N < 16).  A wave's vector memory operations complete in the
+// order they were issued, so all but the N most recent are then done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // LDS of the persistent kernel: the tile buffers, two window tables (the
 // current unit's and the next one's) and, per wave, a staging area for the
@@ -746,7 +768,8 @@ struct PersistLayout {
   using TL = Tiles<D, NW, 1, KT>;
   // two K and two V tile buffers: padded K and transposed V, or (DMA) four
   // row-major swizzled tiles
-  static constexpr int tileBytes = DMA ? 4 * KT * D * 2 : TL::tileBytes;
+  static constexpr int KD = DMA ? BASA_K_DEPTH : 2;   // K tile buffers
+  static constexpr int tileBytes = DMA ? (KD + 2) * KT * D * 2 : TL::tileBytes;
   static constexpr int CPR = D / 8;        // 16B chunks per Q row
   static constexpr int RPI = 64 / CPR;     // Q rows per load instruction (64 lanes x 16B)
   static constexpr int QI = 32 / RPI;      // instructions per wave and unit
@@ -831,9 +854,21 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
   // key tiles of positions 0 and 1 (the same for every unit)
   const int kt0 = kt_of(0), kt1 = kt_of(1);
   unsigned char* tables = smem + PL::tileBytes;
-  // DMA tile buffers: K buffer b at b * kTileB, V buffer b at (2 + b) * kTileB
+  // DMA tile buffers: K buffer b at b * kTileB (b < KD), V buffer b at
+  // (KD + b) * kTileB.  The K tiles of all units of this workgroup go through
+  // the K buffers in turn: position t of a unit whose position 0 went to
+  // buffer kb0 uses buffer (kb0 + t) mod KD, and positions past the unit's
+  // last tile are the next unit's first ones (its kb0 is (kb0 + nkt) mod KD).
+  // V buffers go by the parity of the position (nkt is even).
+  constexpr int KD = PL::KD;
+  static_assert(DMA || KD == 2, "registers-staged tiles use two K buffers");
   auto dK = [&](int b) __attribute__((always_inline)) { return smem + b * C::kTileB; };
-  auto dV = [&](int b) __attribute__((always_inline)) { return smem + (2 + b) * C::kTileB; };
+  auto dV = [&](int b) __attribute__((always_inline)) { return smem + (KD + b) * C::kTileB; };
+  int kb0 = 0;
+  auto kslot = [&](int pos) __attribute__((always_inline)) {
+    if constexpr (KD == 2) return pos & 1;
+    else return (kb0 + pos) % KD;
+  };
   auto get_v = [&](const Unit& u, const uint32_t* tb, int tile) __attribute__((always_inline)) {
     if constexpr (DMA) c.dma_tile(dV(tile & 1), u, tb, tile, true);
     else c.load_v(u, tb, tile);
@@ -900,6 +935,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     c.dma_tile(dK(0), uc, tab_of(0), kt0, false);
     c.dma_tile(dV(0), uc, tab_of(0), kt0, true);
     c.dma_tile(dK(1), uc, tab_of(0), kt1, false);
+    if constexpr (KD == 3) c.dma_tile(dK(2), uc, tab_of(0), kt_of(2), false);
     wait_vmem();
   } else {
     u32x4 k1[TL::KPASS];
@@ -910,7 +946,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     c.store_v(0);
     c.store_k_from(k1, 1);
   }
-  lds_barrier();  // tiles 0 and 1 of unit 0 are in LDS
+  lds_barrier();  // K tiles 0 .. KD-1 and V tile 0 of unit 0 are in LDS
   Scores sA, sB;
   scores(0, sA);
   auto copy = [&](Scores& dst, const Scores& src) __attribute__((always_inline)) {
@@ -933,7 +969,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       if (c.tmask == 0) c.mask_s(sA, 0);
       c.rowmax_all(sA, mx);
       mx[0] += bias_of(0);
-      c.update_max(mx);
+      c.start_max(mx);
     }
     if constexpr (!DMA) {
       c.load_v(uc, tab, kt1);
@@ -945,7 +981,8 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     // loads into LDS go out only after this barrier: until then other waves
     // may still read the buffers (the previous unit's last V tile).
     lds_barrier();
-    if constexpr (DMA) c.dma_pair(true, dV(1), uc, tab, kt1, true, dK(0), uc, tab, kt_of(2));
+    if constexpr (DMA)
+      c.dma_pair(true, dV(1), uc, tab, kt1, true, dK(kslot(KD)), uc, tab, kt_of(KD));
     if (!FULL && j >= 1 && has_next) c.build_table(tab_of(j + 1), un.win);
 
     // Iteration t: as in the unit kernel; the loads past the unit's last tile
@@ -953,7 +990,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     auto iter = [&](int t, Scores& sc, Scores& sn, auto masked) __attribute__((always_inline)) {
       Probs pb;
       float mxn[1];
-      scores((t + 1) & 1, sn);
+      scores(kslot(t + 1), sn);
       c.make_p(sc, pb, bias_of(t) * c.c1);
       if constexpr (DMA) c.pv_dma(dV(t & 1), pb);
       else c.pv(c.sV(t & 1), pb);
@@ -961,22 +998,37 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
       c.rowmax_all(sn, mxn);
       mxn[0] += bias_of(t + 1);
       if constexpr (DMA) {
-        wait_vmem();  // this wave's loads of V(t+1) and K(t+2)
+        // this wave's loads of V(t+1) and K(t+2) (issued in iteration t-1,
+        // or before the unit's first iteration); with three K buffers the
+        // most recent K tile load (K(t+3), issued last in iteration t-1, if
+        // any) may stay in flight
+        if constexpr (KD == 3) {
+          if (t + 3 < nkt || has_next) wait_vmem_but<C::kDmaIpw>();
+          else wait_vmem();
+        } else {
+          wait_vmem();
+        }
       } else {
         c.store_v((t + 1) & 1);
         c.store_k(t & 1);
       }
       lds_barrier();
-      const int tv = t + 2, tk = t + 3;
+      const int tv = t + 2, tk = t + 1 + KD;
       const bool do_v = tv < nkt || (has_next && tv == nkt);
-      const bool do_k = tk < nkt || (has_next && tk <= nkt + 1);
+      const bool do_k = tk < nkt || (has_next && tk < nkt + KD);
       if constexpr (DMA) {
+        // the next unit's Q staging loads go out first, so that the K tile
+        // load is this iteration's last (the wait above relies on it)
+        if (has_next && t < qstep)
+          if constexpr (BASA_PERSISTENT_QSTAGE) {
+            for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
+          }
         const bool cv = tv < nkt, ck = tk < nkt;
         const int jv = cv ? tv : 0, jk = ck ? tk : tk - nkt;
         const Unit u_v = cv ? uc : un;  // by value: the choice stays in registers
         const Unit u_k = ck ? uc : un;
         if (do_v || do_k)
-          c.dma_pair(do_v, dV(jv & 1), u_v, cv ? tab : tabn, kt_of(jv), do_k, dK(jk & 1), u_k,
+          c.dma_pair(do_v, dV(jv & 1), u_v, cv ? tab : tabn, kt_of(jv), do_k, dK(kslot(tk)), u_k,
                      ck ? tab : tabn, kt_of(jk));
       } else {
         if (do_v) {
@@ -990,10 +1042,12 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
           get_k(u, cur ? tab : tabn, kt_of(cur ? tk : tk - nkt));
         }
       }
-      if (has_next && t < qstep)
-        if constexpr (BASA_PERSISTENT_QSTAGE) {
-          for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
-        }
+      if constexpr (!DMA) {
+        if (has_next && t < qstep)
+          if constexpr (BASA_PERSISTENT_QSTAGE) {
+            for (int i = t; i < PL::QI; i += qstep) stage_q(un, tabn, i);
+          }
+      }
       c.update_max(mxn);
     };
     int t = 0;
@@ -1032,17 +1086,21 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     // stages and reads only its own rows).  Its first scores are formed
     // before this unit's output stores are issued, so no wait for a load
     // covers those stores.
-    wait_vmem();
+    // With three K buffers the next unit's K tile 2, issued last, may stay in
+    // flight: its first iteration waits for it.
+    if constexpr (KD == 3) wait_vmem_but<C::kDmaIpw>();
+    else wait_vmem();
     if constexpr (BASA_PERSISTENT_QSTAGE) unstage_q();
     else load_q_of(un, tabn);
     if constexpr (!DMA) {
       c.store_v(0);
       c.store_k(1);
     }
-    scores(0, sA);
+    scores(kslot(nkt), sA);
     finish_of(uc, tab);
     uc = un;
     un = unit_at(j + 2);
+    if constexpr (KD == 3) kb0 = (kb0 + nkt) % KD;
   }
 }
 

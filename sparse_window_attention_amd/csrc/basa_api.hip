@@ -313,6 +313,8 @@ int window_attn_impl(const void* q, const void* k, const void* v, const void* k_
     geo.sx = ((s[2] % w[2]) + w[2]) % w[2];
     geo.nwy = g[1] / w[1];
     geo.nwx = g[2] / w[2];
+    geo.mwx = basa::magic_of(w[2]);
+    geo.mwy = basa::magic_of(w[1]);
     rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, false, (hipStream_t)stream)
                             : basa::launch_attn_f32(p, false, (hipStream_t)stream);
     if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");
@@ -509,6 +511,8 @@ int window_attn_bwd_impl(const void* q, const void* k, const void* v, const void
     geo.sx = ((s[2] % w[2]) + w[2]) % w[2];
     geo.nwy = g[1] / w[1];
     geo.nwx = g[2] / w[2];
+    geo.mwx = basa::magic_of(w[2]);
+    geo.mwy = basa::magic_of(w[1]);
     p.pt = pl[0]; p.py = pl[1]; p.px = pl[2];
     p.Gy = g[1] / pl[1]; p.Gx = g[2] / pl[2];
     rc = basa::launch_attn_bwd(p, (hipStream_t)stream);
@@ -678,6 +682,8 @@ int basa_curve_attn(const void* q, const void* k, const void* v, const void* k_m
     geo.T = 1; geo.Hg = p.nW; geo.Wg = tile;
     geo.wt = 1; geo.wy = 1; geo.wx = tile;
     geo.nwy = p.nW; geo.nwx = 1;
+    geo.mwx = basa::magic_of(tile);
+    geo.mwy = basa::magic_of(1);
     rc = dtype == BASA_BF16 ? basa::launch_attn_bf16(p, false, (hipStream_t)stream)
                             : basa::launch_attn_f32(p, false, (hipStream_t)stream);
     if (rc == BASA_ERR_UNSUPPORTED) return fail(rc, "launch shape not supported");

@@ -23,16 +23,29 @@ struct Geometry {
   int32_t wt, wy, wx;       // window
   int32_t st, sy, sx;       // shift, already reduced into [0, window)
   int32_t nwy, nwx;         // windows along y and x
+  uint32_t mwx, mwy;        // div_magic multipliers of wx and wy
 };
+
+// Multiplier for div_magic: floor((2^32 - 1) / d) + 1, or 0 for d = 1.
+__host__ __device__ inline uint32_t magic_of(int32_t d) {
+  return d <= 1 ? 0u : (uint32_t)(0xFFFFFFFFull / (uint32_t)d + 1ull);
+}
+
+// floor(x / d) as the high half of x * magic_of(d): exact for 0 <= x < 4096
+// and 1 <= d <= 4096 (every slot index of a window, every window dimension;
+// checked exhaustively on the CPU).
+__device__ __forceinline__ int32_t div_magic(int32_t x, uint32_t magic) {
+  return magic ? (int32_t)__umulhi((uint32_t)x, magic) : x;
+}
 
 // Raster index of slot r of window j under the shifted partition: the grid
 // rolled by -shift, cut into windows, window j holds the tokens at
 // (j_axis*w_axis + r_axis + s_axis) mod grid_axis.
 __device__ __forceinline__ int32_t window_token(const Geometry& g, int32_t j, int32_t r) {
-  const int32_t rx = r % g.wx;
-  const int32_t rq = r / g.wx;
-  const int32_t ry = rq % g.wy;
-  const int32_t rt = rq / g.wy;
+  const int32_t rq = div_magic(r, g.mwx);
+  const int32_t rx = r - rq * g.wx;
+  const int32_t rt = div_magic(rq, g.mwy);
+  const int32_t ry = rq - rt * g.wy;
   const int32_t jx = j % g.nwx;
   const int32_t jq = j / g.nwx;
   const int32_t jy = jq % g.nwy;
