@@ -36,6 +36,19 @@ KERNEL_SOURCES = ["sparse_window_attention_amd/csrc/attn_bf16.hip",
                   "sparse_window_attention_amd/csrc/basa_common.h"]
 
 
+# Workloads of --only profile: (workload name in workloads/, kernels run).
+PROFILE_WORKLOADS = {
+    "flux2048_w16": ("FLUX2048_W16", "window"),
+    "flux2048_w32": ("FLUX2048_W32", "window"),
+    "flux1024": ("FLUX1024", "window"),
+    "wan": ("WAN", "window"),
+    "wan_g1638": ("WAN_G1638", "window"),
+    "ultra": ("ULTRA", "window"),
+    "dense_flux2048": ("FLUX2048_W16", "dense"),
+    "backward_flux2048_w16": ("FLUX2048_W16", "backward"),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,11 +61,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--only", choices=("window", "dense", "copy", "backward", "hilbert", "calib",
-                                       "video", "all"),
+                                       "video", "pool", "profile", "all"),
                     default="all",
                     help="'window': only the headline steps; 'dense': only the dense kernel "
                          "at the same shape; 'copy': a plain device copy of known size, the "
                          "calibration for hardware byte counters (all three for profilers)")
+    ap.add_argument("--shapes", default="flux1024,wan,wan_g1638,ultra,tiny_f32",
+                    help="with --only video: comma-separated shapes to time")
+    ap.add_argument("--workload", choices=tuple(PROFILE_WORKLOADS), default="flux2048_w16",
+                    help="with --only profile: the workload whose kernels a few calls run "
+                         "(for a counter profiler)")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="no GPU: read the rocprofv3 counter runs DIR/<workload>/<pass>/ and "
+                         "DIR/copy/{fetch,write}/ and print one markdown table per workload")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="no GPU: read rocprofv3 outputs under DIR (ktrace/, pmc_fetch/, "
                          "pmc_write/, pmc_copy_fetch/, pmc_copy_write/), write the calibrated "
@@ -371,6 +392,83 @@ def summarize_profiles(root):
                       f"max_us {float(r['MaxNs']) / 1e3:9.2f} pct {float(r['Percentage']):6.2f}")
 
 
+COUNTER_PASSES = {
+    "inst": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES "
+            "SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE",
+    "busy": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_LDS "
+            "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
+    "l2": "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+
+
+def _algorithmic(name, kernel):
+    """(flops, read bytes, write bytes) the method needs for one dispatch of
+    `kernel` in profile workload `name` (None where no clean split exists)."""
+    import workloads as W
+    wl = getattr(W, PROFILE_WORKLOADS[name][0])
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    m, G = wl.window_tokens, wl.mem_tokens
+    t = B * H * n * D * 2
+    if "pool_kernel" in kernel:
+        return 0, 2 * t, 2 * B * H * G * D * 2
+    import re
+    full = re.search(r"attn_bf16\w*<\d+, (true|false)", kernel)
+    if full and full.group(1) == "true":
+        return dense_flops(B, H, n, D), 3 * t, t
+    if full:
+        return window_flops(B, H, n, m, G, D), 3 * t + 2 * B * H * G * D * 2, t
+    return None
+
+
+def summarize_counters(root):
+    """Markdown tables of the counter runs under root (see COUNTER_PASSES and
+    --only profile), one per workload: per kernel and dispatch, the MFMA
+    products and their flops against the algorithmic flops, the share of
+    cycles the matrix cores are busy, VALU instructions per MFMA, LDS bank
+    conflicts, L2 hit rate, and HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by
+    what they read for a plain copy of COPY_BYTES) against the algorithmic
+    bytes."""
+    cf = _pick(_counter_means(os.path.join(root, "copy", "fetch"), "FETCH_SIZE"), "copy")[1]
+    cw = _pick(_counter_means(os.path.join(root, "copy", "write"), "WRITE_SIZE"), "copy")[1]
+    fs, ws = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    print(f"copy calibration: FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}\n")
+    for name in PROFILE_WORKLOADS:
+        d = os.path.join(root, name)
+        if not os.path.isdir(d):
+            continue
+        c = {}
+        for ps, ctrs in COUNTER_PASSES.items():
+            for ctr in ctrs.split():
+                for k, val in _counter_means(os.path.join(d, ps), ctr).items():
+                    c.setdefault(k, {})[ctr] = val
+        print(f"### {name}\n")
+        print("| kernel | MFMA | MFMA GFLOP (algorithmic) | MFMA busy | VALU / MFMA | "
+              "LDS conflicts / LDS inst | L2 hit | HBM read MB (algorithmic) | "
+              "HBM write MB (algorithmic) |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for k in sorted(c):
+            v = c[k]
+            grbm = v.get("GRBM_GUI_ACTIVE", 0.0)
+            mf = v.get("SQ_INSTS_MFMA", 0.0)
+            busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * grbm / 8) if grbm else 0.0
+            alg = _algorithmic(name, k)
+            af = f" ({alg[0] / 1e9:.2f})" if alg and alg[0] else ""
+            ar = f" ({alg[1] / 1e6:.1f})" if alg else ""
+            aw = f" ({alg[2] / 1e6:.1f})" if alg else ""
+            hits = v.get("TCC_HIT_sum", 0.0)
+            miss = v.get("TCC_MISS_sum", 0.0)
+            lds = v.get("SQ_ACTIVE_INST_LDS", 0.0)
+            print(f"| {k[:60]} | {mf:.4g} | {mf * 32768 / 1e9:.2f}{af} | {busy:.1%} | "
+                  f"{v.get('SQ_INSTS_VALU', 0.0) / mf if mf else 0.0:.2f} | "
+                  f"{v.get('SQ_LDS_BANK_CONFLICT', 0.0) / lds if lds else 0.0:.3f} | "
+                  f"{hits / (hits + miss) if hits + miss else 0.0:.1%} | "
+                  f"{v.get('FETCH_SIZE', 0.0) * 1024 * fs / 1e6:.1f}{ar} | "
+                  f"{v.get('WRITE_SIZE', 0.0) * 1024 * ws / 1e6:.1f}{aw} |")
+        print()
+
+
 def median(x):
     x = sorted(x)
     return x[len(x) // 2] if len(x) % 2 else 0.5 * (x[len(x) // 2 - 1] + x[len(x) // 2])
@@ -668,6 +766,113 @@ def measure_other_shape(S, wl, stream, dev, steps, dense_reps):
     return r
 
 
+def run_profile_workload(S, name, stream, dev, calls=3):
+    """A few calls of one workload's kernels on N(0,1) inputs drawn on the
+    GPU, for a counter profiler (every dispatch is averaged)."""
+    import torch
+    import workloads as W
+    wl = getattr(W, PROFILE_WORKLOADS[name][0])
+    kind = PROFILE_WORKLOADS[name][1]
+    B, H, n, D = wl.batch, wl.heads, wl.n_tokens, wl.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000)
+    q, k, v = (torch.randn((B, H, n, D), generator=g, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty_like(q)
+    for i in range(calls):
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        if kind == "dense":
+            S.full_attn(q, k, v, out=out)
+        elif kind == "window":
+            mem = S.pool_kv(k, v, wl.grid, wl.pool)
+            S.window_attn(q, k, v, wl.grid, wl.window, shift, mem=mem, out=out)
+        else:
+            mem = S.pool_kv(k, v, wl.grid, wl.pool)
+            o, lse = S.window_attn_fwd(q, k, v, wl.grid, wl.window, shift, mem=mem, out=out)
+            S.window_attn_bwd(q, k, v, o, q, lse, wl.grid, wl.window, shift, mem=mem,
+                              pool=wl.pool)
+        torch.cuda.synchronize()
+    return {"workload": name, "calls": calls}
+
+
+def measure_pool(S, stream, dev, steps):
+    """The pool at FLUX-2048 (24 heads, 8x8 cells) two ways: alone (the GPU
+    idle before each call) and in the step (right after a window attention
+    launch, whose 100 MB of output is still being written)."""
+    import torch
+    import workloads as W
+    wl = W.FLUX2048_W16
+    B, H, n, D, G = wl.batch, wl.heads, wl.n_tokens, wl.head_dim, wl.mem_tokens
+    sets = make_sets(wl, 5, dev)
+    mem = tuple(torch.empty((B, H, G, D), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    out = torch.empty_like(sets[0][0])
+    alone, instep = [], []
+    c = 0   # each call takes the next of the 5 input sets: no call finds its
+            # inputs in the last-level cache from the call before
+    for i in range(steps + 2):
+        shift = S.shift_for_block(i % 4, wl.schedule, wl.window)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        _queue_backlog(0.001, stream)
+        ev[0].record(stream)
+        q, k, v = sets[c % len(sets)]
+        S.pool_kv(k, v, wl.grid, wl.pool, out=mem)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        _queue_backlog(0.001, stream)
+        q, k, v = sets[(c + 1) % len(sets)]
+        S.window_attn(q, k, v, wl.grid, wl.window, shift, mem=mem, out=out)
+        ev[2].record(stream)
+        q, k, v = sets[(c + 2) % len(sets)]
+        S.pool_kv(k, v, wl.grid, wl.pool, out=mem)
+        ev[3].record(stream)
+        c += 3
+        torch.cuda.synchronize()
+        if i >= 2:
+            alone.append(ev[0].elapsed_time(ev[1]))
+            instep.append(ev[2].elapsed_time(ev[3]))
+    byts = 2 * B * H * n * D * 2 + 2 * B * H * G * D * 2
+    a, b = median(alone), median(instep)
+    return {"workload": wl.name, "pool_alone_ms": a, "pool_in_step_ms": b,
+            "algorithmic_bytes": byts, "alone_gbs": byts / (a * 1e-3) / 1e9,
+            "in_step_gbs": byts / (b * 1e-3) / 1e9,
+            "note": "alone: after the GPU idled (synchronised), behind a short backlog; in "
+                    "step: launched right after a window attention call; every call on an "
+                    "input set not touched by the two calls before it"}
+
+
+def measure_tiny(S, stream, dev, steps):
+    """The fp32 Tiny workload (16x16 tokens, one head, D = 64, 8x8 windows
+    shifted by (4,4), no memory) through the fp32 kernels, and the fp32 dense
+    kernel at the same shape; each call queued behind a short backlog."""
+    import torch
+    import workloads as W
+    wl = W.TINY
+    q, k, v = (torch.from_numpy(x).to(dev) for x in W.make_qkv(wl))
+    out = torch.empty_like(q)
+    win, dense = [], []
+    for i in range(steps + 3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        _queue_backlog(0.001, stream)
+        ev[0].record(stream)
+        S.window_attn(q, k, v, wl.grid, wl.window, (4, 4), scale=1.0 / math.sqrt(64), out=out)
+        ev[1].record(stream)
+        S.full_attn(q, k, v, out=out)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            win.append(ev[0].elapsed_time(ev[1]))
+            dense.append(ev[1].elapsed_time(ev[2]))
+    n, m, D = wl.n_tokens, wl.window_tokens, wl.head_dim
+    w_ms, d_ms = median(win), median(dense)
+    return {"workload": wl.name, "dtype": "f32", "n": n, "m": m, "G": 0,
+            "window_attn_ms": w_ms,
+            "window_attn_gflops": window_flops(1, 1, n, m, 0, D) / (w_ms * 1e-3) / 1e9,
+            "dense_ms": d_ms, "realised_over_theoretical": d_ms / w_ms / (n / m),
+            "note": "fp32 vector-ALU kernels (an accuracy path, not a throughput one): one "
+                    "workgroup per 128 queries, so a call is launch- and latency-bound"}
+
+
 HILBERT_SIDES = (64, 128)    # token grids of 1024 x 1024 and 2048 x 2048 px images
 HILBERT_TILE = 256
 HILBERT_REGION = (8, 8)
@@ -696,6 +901,7 @@ def measure_hilbert(S, stream, dev, steps):
             q, k, v = sets[i % 2]
             slide = (i % 2) * HILBERT_TILE // 2
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            _queue_backlog(0.002, stream)   # the step's launches are issued before it runs
             ev[0].record(stream)
             S.gather_kv(k, v, reg, out=mem)
             ev[1].record(stream)
@@ -815,6 +1021,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
         return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -845,9 +1054,21 @@ def main():
         print(json.dumps(measure_backward(S, head, sets, args.steps, stream)))
         return
     if args.only == "video":
-        print(json.dumps({"wan": measure_other_shape(S, W.WAN, stream, dev, args.steps, 3),
-                          "ultra": measure_other_shape(S, W.ULTRA, stream, dev,
-                                                       max(4, args.steps // 4), 2)}))
+        runs = {"wan": lambda: measure_other_shape(S, W.WAN, stream, dev, args.steps, 3),
+                "wan_g1638": lambda: measure_other_shape(S, W.WAN_G1638, stream, dev,
+                                                         args.steps, 3),
+                "ultra": lambda: measure_other_shape(S, W.ULTRA, stream, dev,
+                                                     max(4, args.steps // 4), 3),
+                "flux1024": lambda: measure_other_shape(S, W.FLUX1024, stream, dev,
+                                                        args.steps, 5),
+                "tiny_f32": lambda: measure_tiny(S, stream, dev, args.steps)}
+        print(json.dumps({k: runs[k]() for k in args.shapes.split(",")}))
+        return
+    if args.only == "profile":
+        print(json.dumps(run_profile_workload(S, args.workload, stream, dev)))
+        return
+    if args.only == "pool":
+        print(json.dumps(measure_pool(S, stream, dev, args.steps)))
         return
     if args.only == "calib":
         print(json.dumps(measure_mfma_peak(S, stream)))
@@ -892,7 +1113,10 @@ def main():
     wan = measure_other_shape(S, W.WAN, stream, dev, max(8, args.steps // 4), 3)
     wan["pages_context"] = ("up to 4.52x attention speedup on Wan (the pages' own dense baseline "
                             "and hardware, not stated)")
-    ultra = measure_other_shape(S, W.ULTRA, stream, dev, 4, 2)
+    wan1638 = measure_other_shape(S, W.WAN_G1638, stream, dev, max(8, args.steps // 4), 3)
+    ultra = measure_other_shape(S, W.ULTRA, stream, dev, 4, 3)
+    flux1024 = measure_other_shape(S, W.FLUX1024, stream, dev, max(8, args.steps // 2), 5)
+    tiny = measure_tiny(S, stream, dev, max(8, args.steps // 2))
     print(f"[bench] wan: attn {wan['window_attn_ms']*1e3:.0f} us ({wan['window_attn_tflops']:.0f} "
           f"TFLOP/s), dense {wan['dense_ms']:.2f} ms; ultra: attn {ultra['window_attn_ms']:.2f} ms, "
           f"dense {ultra['dense_ms']:.0f} ms", file=sys.stderr, flush=True)
@@ -951,7 +1175,8 @@ def main():
         "backward": bwd,
         "hilbert_tiles": hil,
         "mfma_calibration": calib,
-        "other_shapes": {"wan": wan, "ultra": ultra},
+        "other_shapes": {"flux1024": flux1024, "wan": wan, "wan_g1638": wan1638,
+                         "ultra": ultra, "tiny_f32": tiny},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -88,9 +88,14 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
     float mt = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kKT; ++j) {
-      float dot = 0.0f;
+      // four independent partial sums: a chain of D dependent fmas per key
+      // would leave the ALU waiting on each one's result
+      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(q[d], sK[j * D + d], dot);
+      for (int d = 0; d < D; d += 4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d4[e] = __builtin_fmaf(q[d + e], sK[j * D + d + e], d4[e]);
+      const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
       float x = dot * scale;
       if (k0 + j >= nwin) x += p.mem_bias;
       s[j] = (j < nk) ? x : -INFINITY;
