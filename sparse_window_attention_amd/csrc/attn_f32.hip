@@ -5,7 +5,8 @@
 // one query row, keeps q and its output accumulator in registers, and walks
 // the key tiles staged in LDS (every thread reads the same key row, an LDS
 // broadcast).  Softmax in natural-log units with expf, exact rescale per
-// tile.  Built for accuracy on small fp32 workloads, not for speed.
+// group of 2 (D = 128) or 8 (D = 64) keys.  Built for accuracy on small fp32
+// workloads, not for speed.
 #include "basa_common.h"
 #include "basa_internal.h"
 
@@ -14,7 +15,11 @@ namespace basa {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kKT = 32;
+constexpr int kKT = 32;   // keys per LDS tile
+// keys scored and folded in at a time: q and the accumulator already hold
+// 2*D registers per thread
+template <int D>
+constexpr int kSub = D >= 128 ? 2 : 8;
 
 template <int D, bool FULL>
 __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
@@ -84,35 +89,47 @@ __global__ void __launch_bounds__(kThreads) attn_f32_kernel(AttnParams p) {
     }
     __syncthreads();
     const int nk = min(kKT, L - k0);
-    float s[kKT];
-    float mt = -INFINITY;
+    // groups of kSub keys: scores, the exact rescale of the running sum and
+    // accumulator to the new max, then P V; a group of padding keys only is
+    // skipped (keys past L come last, so one of them ends the tile)
+#pragma unroll 1
+    for (int j0 = 0; j0 < nk; j0 += kSub<D>) {
+      float s[kSub<D>];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kKT; ++j) {
-      // four independent partial sums: a chain of D dependent fmas per key
-      // would leave the ALU waiting on each one's result
-      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int jj = 0; jj < kSub<D>; ++jj) {
+        const int j = j0 + jj;
+        // four independent partial sums of the dot product
+        float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int d = 0; d < D; d += 4)
+        for (int d = 0; d < D; d += 4) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(sK + j * D + d);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d4[e] = __builtin_fmaf(q[d + e], sK[j * D + d + e], d4[e]);
-      const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-      float x = dot * scale;
-      if (k0 + j >= nwin) x += p.mem_bias;
-      s[j] = (j < nk) ? x : -INFINITY;
-      mt = fmaxf(mt, s[j]);
-    }
-    const float mnew = fmaxf(mrun, mt);
-    const float alpha = expf(mrun - mnew);
-    mrun = mnew;
-    lsum *= alpha;
+          for (int e = 0; e < 4; ++e) d4[e] = __builtin_fmaf(q[d + e], kv[e], d4[e]);
+        }
+        float x = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * scale;
+        if (k0 + j >= nwin) x += p.mem_bias;
+        s[jj] = (j < nk) ? x : -INFINITY;
+        mt = fmaxf(mt, s[jj]);
+      }
+      const float mnew = fmaxf(mrun, mt);   // finite: the group holds a valid key
+      const float alpha = expf(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+      for (int d = 0; d < D; ++d) acc[d] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kKT; ++j) {
-      const float pj = expf(s[j] - mnew);
-      lsum += pj;
+      for (int jj = 0; jj < kSub<D>; ++jj) {
+        const float pj = expf(s[jj] - mnew);
+        lsum += pj;
+        const float* vr = sV + (j0 + jj) * D;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(pj, sV[j * D + d], acc[d]);
+        for (int d = 0; d < D; d += 4) {
+          const f32x4 vv = *reinterpret_cast<const f32x4*>(vr + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[d + e] = __builtin_fmaf(pj, vv[e], acc[d + e]);
+        }
+      }
     }
   }
   if (qvalid) {
