@@ -46,6 +46,7 @@ namespace basa {
 namespace {
 
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
+constexpr int kStoreNT = 2;            // cache policy of buffer stores: non-temporal
 constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel needs
 // Persistent kernel: LDS operand reads this many MFMA steps ahead (score
 // product, P V product).
@@ -625,6 +626,56 @@ struct Core {
         if (qvalid) __builtin_amdgcn_raw_buffer_store_b128(w, rs, qoff + d * 2, 0, 0);
       }
   }
+  // The same through this wave's 32-row staging area (stage: row r's 16-byte
+  // chunk c at slot c ^ (r % CPR), the Q staging layout): the rows are
+  // written there, then read back so that each store instruction writes
+  // 64 / CPR whole rows, with the non-temporal policy.  Whole-row stores
+  // need no merging in L2, and the output (not read again here) then drains
+  // to HBM while the kernel still runs.
+  __device__ __forceinline__ void finish_lds(const Unit& u, int qb, uint32_t qoff, bool qvalid,
+                                             unsigned char* stage) const {
+    const float lp = l0[qb] + l1[qb];
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
+                                                     false, false);
+    const float lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float inv = 1.0f / lsum;
+    if (p.lse != nullptr && qvalid && hf == 0) {
+      const uint32_t token = qoff / stb;
+      p.lse[(int64_t)u.bh * p.n_tok + token] = (m_used[qb] + __builtin_log2f(lsum)) * 0.6931471805599453f;
+    }
+    constexpr int CPR = TL::CPR;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; g += 2) {
+        const uint32_t a0 = pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv);
+        const uint32_t a1 = pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
+        const uint32_t b0 =
+            pack_bf16x2(acc[qb][db][4 * g + 4] * inv, acc[qb][db][4 * g + 5] * inv);
+        const uint32_t b1 =
+            pack_bf16x2(acc[qb][db][4 * g + 6] * inv, acc[qb][db][4 * g + 7] * inv);
+        const auto x0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+        const u32x4 w{x0[0], x1[0], x0[1], x1[1]};
+        const int ch = db * 4 + g + 1 - hf;   // d = 8 ch .. 8 ch + 7 of row l32
+        *reinterpret_cast<u32x4*>(stage + (l32 * CPR + (ch ^ (l32 % CPR))) * 16) = w;
+      }
+    // a wave's LDS accesses complete in order, so the reads below see the
+    // writes; the wave barrier keeps the compiler from moving them across
+    __builtin_amdgcn_wave_barrier();
+    const Rsrc rs = make_rsrc(p.out + u.base);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int r = (64 / CPR) * i + lane / CPR;
+      const int ch = (lane % CPR) ^ (r % CPR);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + i * 1024 + lane * 16);
+      // row r's offset and validity from lane r (rows 0-31 sit in lanes 0-31)
+      const uint32_t ro = (uint32_t)__builtin_amdgcn_ds_bpermute(r * 4, (int)qoff);
+      const int rv = __builtin_amdgcn_ds_bpermute(r * 4, qvalid ? 1 : 0);
+      if (rv) __builtin_amdgcn_raw_buffer_store_b128(w, rs, ro + (uint32_t)ch * 16u, 0, kStoreNT);
+    }
+  }
 };
 
 // One workgroup per work unit.
@@ -916,10 +967,13 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
           qstage + (c.l32 * PL::CPR + (ch ^ (c.l32 % PL::CPR))) * 16);
     }
   };
+  // the output rows go out through the wave's staging area, free from the
+  // read of the next unit's Q rows until the next unit's first staging load
   auto finish_of = [&](const Unit& u, const uint32_t* tb) __attribute__((always_inline)) {
     const int r = c.qrow(u, 0);
     const bool valid = r < c.m;
-    c.finish(u, 0, valid ? c.tok(tb, r) : 0u, valid);
+    if constexpr (BASA_PERSISTENT_QSTAGE) c.finish_lds(u, 0, valid ? c.tok(tb, r) : 0u, valid, qstage);
+    else c.finish(u, 0, valid ? c.tok(tb, r) : 0u, valid);
   };
 
   // ---- unit 0: tables of units 0 and 1; its operands from global memory

@@ -23,6 +23,9 @@ queue of vector memory operations:
 * a wave's own Q staging area and the per-unit token tables follow the same
   rules (the staging area is private to the wave, so its loads need only
   the wave's own wait before the read);
+* the output rows of a unit pass through the wave's staging area (written
+  and read back by the wave) after the next unit's Q rows have been read
+  from it, so no staging load may be in flight into it then;
 * no load or table read ever names a unit past the workgroup's last one.
 
 It is the schedule's specification on the CPU; the kernel runs the same
@@ -99,6 +102,14 @@ class Model:
         self.pending.pop(buf, None)
         self.last_read[buf] = self.seg
         self.reads.append((kind, content))
+
+    # the wave's own staging area as scratch: no load into it may be in flight
+    def use_private(self, buf, kind):
+        if any(b == buf for b, _ in self.queue):
+            raise Violation(f"{kind}: staging area reused with a load into it in flight")
+        if self.pending.get(buf) is not None and any(b == buf for b, _ in self.completed):
+            raise Violation(f"{kind}: staging area reused before its loaded rows were read")
+        self.last_read[buf] = self.seg
 
     def write_table(self, slot, unit):
         buf = ("tab", slot)
@@ -187,6 +198,8 @@ def run_schedule(nkt, J, KD, ipw=2, QI=8):
         M.read(V(t % 2), ("V", uc, t), f"PV({t})")
         if not has_next:
             M.read_table(uc % 2, uc, "output rows")
+            for i in range(QI):
+                M.use_private(("Q", i), "output staging")
             M.store(8)
             break
         M.wait(ipw if KD == 3 else 0)
@@ -194,6 +207,8 @@ def run_schedule(nkt, J, KD, ipw=2, QI=8):
             M.read_private(("Q", i), ("Q", un, i), "Q of the next unit")
         M.read(K(kslot(nkt)), ("K", un, 0), "S(0) of the next unit")
         M.read_table(uc % 2, uc, "output rows")
+        for i in range(QI):
+            M.use_private(("Q", i), "output staging")
         M.store(8)
         if KD == 3:
             kb0 = (kb0 + nkt) % KD
@@ -238,6 +253,15 @@ def test_model_catches_a_load_into_a_buffer_being_read():
     M.read(("K", 0), ("K", 0, 0), "S(0)")
     with pytest.raises(Violation):
         M.issue(("K", 0), ("K", 0, 2), 2)             # same segment as the read
+
+
+def test_model_catches_output_staging_over_a_staging_load():
+    # the output rows may not go through the staging area while the next
+    # unit's Q rows are still being loaded into it
+    M = Model(8, 2, 2, 2, 8)
+    M.issue(("Q", 0), ("Q", 1, 0))
+    with pytest.raises(Violation, match="output staging"):
+        M.use_private(("Q", 0), "output staging")
 
 
 def test_model_catches_a_load_past_the_last_unit():
