@@ -132,13 +132,26 @@ def test_memory_bias_persistent(case):
 
 
 # ------------------------------------------------------------------ pooling
+# (grid, pool, head dim): a wave's 64 / (16-byte chunks per row) lane groups
+# split each cell row of px tokens, px a multiple of the group count or not
+# (a partial last step); video cells of several frames, image cells, one-row
+# cells, head dims 64 and 128
+POOL_SHAPES = [((6, 20, 24), (3, 5, 4), 128),   # bf16 1 token per group and row, f32 2
+               ((32, 32), (8, 8), 128),         # bf16 2, f32 4
+               ((32, 48), (16, 16), 64),        # bf16 2, f32 4
+               ((12, 15), (3, 5), 128),         # px not a multiple of the groups
+               ((16, 16), (1, 4), 128),         # one row per cell
+               ((2, 8, 12), (2, 2, 6), 64)]     # two frames, px not a multiple
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
-def test_pool_kv(dtype, layout):
-    grid, pool = (6, 20, 24), (3, 5, 4)
-    n, B, H, D = 2880, 2, 2, 128
-    log(f"pool {dtype} {layout}")
-    _, k, v = random_qkv((B, H, n, D), dtype, seed=9)
+@pytest.mark.parametrize("shape", range(len(POOL_SHAPES)))
+def test_pool_kv(dtype, layout, shape):
+    grid, pool, D = POOL_SHAPES[shape]
+    n, B, H = int(np.prod(grid)), 2, 2
+    log(f"pool {dtype} {layout} grid={grid} pool={pool} D={D}")
+    _, k, v = random_qkv((B, H, n, D), dtype, seed=9 + shape)
     conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)
     km, vm = S.pool_kv(to_gpu(conv(k), dtype), to_gpu(conv(v), dtype), grid, pool, layout=layout)
     _sync()
