@@ -24,7 +24,7 @@ def torch_dev():
 def to_gpu(x, dtype):
     """numpy float32 values (exact in dtype) -> GPU tensor of dtype."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = torch.from_numpy(np.array(x, dtype=np.float32, order="C"))   # a writable copy
     t = t.to(torch.bfloat16) if dtype == "bf16" else t
     return t.to(torch_dev())
 
