@@ -28,7 +28,9 @@
 // tiles are loaded into free tile buffers and its Q rows into a per-wave LDS
 // staging area, so the next unit starts from LDS instead of paying a burst
 // of HBM loads; the finished unit's output is stored once the next unit's
-// first scores are formed.
+// first scores are formed, passing through the wave's staging area so that
+// every store writes whole rows (non-temporal: the output drains to HBM while
+// the kernel runs).
 //
 // The cyclic shift and the window gather are address arithmetic: a table of
 // the window's raster offsets is built in LDS per unit and every Q/K/V/O row
