@@ -11,6 +11,10 @@ code does it).
   computed as a multiply by floor((2^32 - 1) / t1) + 1; it must be a
   bijection of [0, t1) that keeps window tiles and other tiles each in
   order, for t1 <= 1024 and nw <= 64.
+* The output rows of the persistent kernel pass through each wave's staging
+  area (attn_bf16.hip: finish_lds): the writes from the accumulator layout
+  and the reads back for whole-row stores must be inverse maps of every
+  (row, 16-byte chunk).
 """
 import numpy as np
 
@@ -55,3 +59,63 @@ def test_interleaved_tile_order_examples():
     show = lambda t1, nw: "".join("W" if k < nw else "m" for k in _tile_order(t1, nw))
     assert show(8, 4) == "WmWmWmWm"            # 16x16 windows, 256 memory tokens
     assert show(20, 16) == "WWWWm" * 4          # 32x32 windows, 256 memory tokens
+
+
+def _staged_output_maps(D):
+    """The persistent kernel's output path (finish_lds): lane (l32, hf) holds,
+    for d block db and group pair g in {0, 2}, the 8 d values of chunk
+    c = 4 db + g + 1 - hf of query row l32 after the lane-pair exchange, and
+    writes them to staging byte (l32 * CPR + (c ^ (l32 % CPR))) * 16.  Store
+    instruction i then reads byte i * 1024 + 16 * lane and writes it to row
+    r = (64 / CPR) i + lane / CPR at byte 16 * ((lane % CPR) ^ (r % CPR))."""
+    CPR, DB = D // 8, D // 32
+    writes = {}
+    for l32 in range(32):
+        for hf in range(2):
+            for db in range(DB):
+                for g in (0, 2):
+                    c = db * 4 + g + 1 - hf
+                    slot = l32 * CPR + (c ^ (l32 % CPR))
+                    assert slot not in writes
+                    writes[slot] = (l32, c)
+    reads = {}
+    for i in range(32 * CPR // 64):
+        for lane in range(64):
+            r = (64 // CPR) * i + lane // CPR
+            ch = (lane % CPR) ^ (r % CPR)
+            slot = (i * 1024 + lane * 16) // 16
+            reads[slot] = (r, ch)
+    return CPR, writes, reads
+
+
+def test_staged_output_transpose_is_exact():
+    for D in (64, 128):
+        CPR, writes, reads = _staged_output_maps(D)
+        # every (row, chunk) of the wave's 32 rows written once, read back once,
+        # and stored at its own row and chunk
+        assert sorted(writes.values()) == [(r, c) for r in range(32) for c in range(CPR)]
+        assert set(writes) == set(reads)
+        for slot, rc in reads.items():
+            assert writes[slot] == rc, (D, slot)
+
+
+def test_staged_output_writes_spread_over_banks():
+    # a b128 LDS access is served 16 lanes at a time; the 16 lanes of each
+    # quarter wave should land in distinct 16-byte slots modulo 256 bytes (the
+    # 64 banks of 4 bytes).  At D = 128 (one row per 256 bytes) the writes do;
+    # at D = 64 rows r and r + 8 share a slot (2-way, on the four writes per
+    # wave and unit).  The reads back are contiguous.
+    for D, distinct in ((64, 8), (128, 16)):
+        CPR, DB = D // 8, D // 32
+        for hf in range(2):
+            for db in range(DB):
+                for g in (0, 2):
+                    c = db * 4 + g + 1 - hf
+                    for q0 in range(0, 32, 16):
+                        banks = [((l32 * CPR + (c ^ (l32 % CPR))) * 16 // 16) % 16
+                                 for l32 in range(q0, q0 + 16)]
+                        assert len(set(banks)) == distinct, (D, hf, db, g, q0)
+        for i in range(32 * CPR // 64):
+            for q in range(4):
+                banks = [((i * 1024 + lane * 16) // 16) % 16 for lane in range(16 * q, 16 * q + 16)]
+                assert len(set(banks)) == 16
