@@ -274,17 +274,32 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
         dp = mfma(b, dreg[ss], dp);
       }
       u32x4 dsb[2];
+      // A tile of window keys only or of memory keys only, with no key past
+      // the end, takes the memory bias as one offset; other tiles select
+      // per key (bias for memory keys, -inf past the end).
+      const int k0 = it * Q::kKeys;
+      const bool whole = k0 + Q::kKeys <= p.m || (k0 >= p.m && k0 + Q::kKeys <= L);
+      const float nb = (k0 >= p.m ? p.mem_bias_raw * c1 : 0.0f) - lse2;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float e[8];
+        if (whole) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * u + j;
-          const int key = it * Q::kKeys + kb * 32 + acc_row(r, hf);
-          float xv = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
-          xv = key < L ? xv : -INFINITY;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(xv, c1, -lse2));
-          e[j] = pr * (dp[r] - dval);
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * u + j;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c1, nb));
+            e[j] = pr * (dp[r] - dval);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * u + j;
+            const int key = k0 + kb * 32 + acc_row(r, hf);
+            float xv = s[r] + (key >= p.m ? p.mem_bias_raw : 0.0f);
+            xv = key < L ? xv : -INFINITY;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(xv, c1, -lse2));
+            e[j] = pr * (dp[r] - dval);
+          }
         }
         dsb[u] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                        pack_bf16x2(e[6], e[7])};
