@@ -429,7 +429,9 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
       const int q = it * kQ + tid;
       const bool ok = q < nq;
       const int64_t idx = (int64_t)bh * p.n + token_of(ok ? q : nq - 1);
-      lx = ok ? p.lse[idx] * kLog2e : INFINITY;   // a missing query gets P = 0
+      // log2-scale log-sum-exp less the memory keys' bias (P = exp2(S c1 -
+      // lx) with the bias folded in); a missing query gets P = 0
+      lx = ok ? p.lse[idx] * kLog2e - (MEM ? p.mem_bias_raw * p.c1 : 0.0f) : INFINITY;
       dvx = ok ? p.dvec[idx] : 0.0f;
     }
   };
@@ -445,7 +447,6 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
   const float c1 = p.c1;
-  const float bias = MEM ? p.mem_bias_raw : 0.0f;
   const int x = Q::swz(l32);
   const int sq = (lane & 15) >> 2;
   const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
@@ -468,7 +469,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + hf * 16 + r4 * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i] + bias, c1, -l4[i]));
+          pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i], c1, -l4[i]));
       }
       float w[16];   // pass 0: P; pass 1: dS
       if constexpr (PASS == 0) {
