@@ -382,6 +382,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   const int key = kbase + wave * 32 + l32;
   const bool kvalid = key < nkeys;
   const int kcl = min(key, nkeys - 1);
+
   u32x4 kreg[T::QS], vreg[PASS == 1 ? T::QS : 1];
   {
     const uint16_t* ks = MEM ? p.kmem + (int64_t)bh * p.G * D : p.k + base;
@@ -444,6 +445,19 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   };
   get(0);
   put(0);
+  // window keys: the pooled-memory cell of the key's token, whose gradient
+  // the epilogue adds; its divisions run while the unit's first loads are
+  // in flight, off the epilogue's path
+  int cell = 0;
+  if constexpr (!MEM) {
+    if (p.G > 0) {
+      const int tok = tab[kcl];
+      const int xx = tok % p.geo.Wg;
+      const int y = (tok / p.geo.Wg) % p.geo.Hg;
+      const int t = tok / (p.geo.Wg * p.geo.Hg);
+      cell = ((t / p.pt) * p.Gy + y / p.py) * p.Gx + xx / p.px;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
   const float c1 = p.c1;
@@ -534,13 +548,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   } else {
     const int tok = tab[kcl];
     const float* add = nullptr;
-    if (p.G > 0) {
-      const int xx = tok % p.geo.Wg;
-      const int y = (tok / p.geo.Wg) % p.geo.Hg;
-      const int t = tok / (p.geo.Wg * p.geo.Hg);
-      const int cell = ((t / p.pt) * p.Gy + y / p.py) * p.Gx + xx / p.px;
-      add = (PASS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
-    }
+    if (p.G > 0) add = (PASS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
     store_rows<D>(acc, PASS == 0 ? 1.0f : p.scale, add, (PASS == 0 ? p.dv : p.dk) + base,
                   (uint32_t)tok * stb, kvalid, hf);
   }
