@@ -46,6 +46,9 @@ CASES = [
     ("bnhd", 2, 2, 128, (16, 32), (8, 16), (4, 9), (4, 8), 0.0, "bnhd"),
     ("query chunks", 1, 2, 128, (32, 48), (16, 16), (8, 8), (8, 8), 0.0, "bhnd"),
     ("window 400", 1, 2, 128, (40, 40), (20, 20), (10, 7), (8, 8), 0.0, "bhnd"),
+    # a 64-key tile holding window keys, memory keys and keys past the end,
+    # with a memory bias (the dQ kernel's per-key path)
+    ("window 400, bias", 1, 2, 128, (40, 40), (20, 20), (10, 7), (8, 8), math.log(64.0), "bhnd"),
     ("memory 1024", 1, 2, 128, (64, 64), (16, 16), (8, 8), (2, 2), 0.0, "bhnd"),
     # the persistent forward with memory-only tiles taking the bias as an offset
     ("memory-only tiles, bias", 1, 2, 128, (64, 64), (16, 16), (8, 3), (4, 4),
