@@ -13,13 +13,15 @@
 // (batch, head), which mean pooling hands on to each token of its cell
 // divided by the cell size.
 //
-// Kernels (one workgroup of 8 waves per unit, XCD-aware unit order):
+// Kernels (one workgroup per unit, 32 rows per wave, XCD-aware unit order):
 //   dvec     Dv for every token
-//   dq       query-stationary: 256 queries of a window against the key
-//            sequence [window keys; memory keys] in tiles of 64 keys loaded
-//            straight into LDS: S^T = K Q^T, dP^T = V dO^T, dS^T,
-//            dQ^T += K^T dS^T (K^T by transposing LDS reads)
-//   dkdv     key-stationary: 256 keys (32 per wave) against blocks of 32
+//   dq       query-stationary: 128 queries of a window (4 waves, two
+//            workgroups per CU) against the key sequence [window keys;
+//            memory keys] in tiles of 64 keys loaded straight into LDS:
+//            S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (K^T by
+//            transposing LDS reads)
+//   dkdv     key-stationary: 128 window keys (4 waves, two workgroups per
+//            CU) or 256 memory keys (8 waves) against blocks of 32
 //            queries: S = Q K^T, P; pass 0: dV^T += dO^T P; pass 1:
 //            dP = dO V^T, dS, dK^T += Q^T dS.  Both passes run in one grid
 //            (one launch for memory keys, one for window keys).  Memory-key
@@ -39,10 +41,23 @@ namespace basa {
 
 namespace {
 
-constexpr int kNW = 8;                 // waves per workgroup
-constexpr int kThreads = kNW * 64;
+constexpr int kNW = 8;                 // waves per workgroup unless a kernel chooses
 constexpr int kBlk = 32;               // rows of one MFMA block: keys (dq), queries (dkdv)
-constexpr int kUnit = kNW * 32;        // queries per dq unit, keys per dkdv unit
+
+// Waves per workgroup of the dQ kernel and of the dK/dV kernel for window
+// keys and for memory keys: 8, or 4 with two workgroups per CU, so that one
+// workgroup's first loads and last stores overlap the other's products
+// (the short units of dQ and of window keys gain; the memory keys' units,
+// four times longer, do not).
+#ifndef BASA_BWD_DQ_WAVES
+#define BASA_BWD_DQ_WAVES 4
+#endif
+#ifndef BASA_BWD_DKDV_WAVES
+#define BASA_BWD_DKDV_WAVES 4
+#endif
+#ifndef BASA_BWD_DKDV_MEM_WAVES
+#define BASA_BWD_DKDV_MEM_WAVES 8
+#endif
 
 template <int D>
 struct BT {
@@ -142,25 +157,28 @@ __global__ void __launch_bounds__(256) bwd_dvec_kernel(BwdParams p) {
 // c ^ f(r), f a bijection of r mod 16 whose bits 2-3 separate any 4
 // consecutive rows, so the 16 rows of a quarter-wave row read and the
 // 4 rows x 4 chunks of a half-wave transposing read fall in distinct banks.
-template <int D>
+template <int D, int NW = kNW>
 struct DqDma {
   using T = BT<D>;
   static constexpr int kKeys = 64;                  // keys per iteration
   static constexpr int CPR = D / 8;
   static constexpr int RowB = CPR * 16;             // bytes per row
   static constexpr int kTileB = kKeys * RowB;       // one K or V tile
-  static constexpr int kIpw = kTileB / 1024 / kNW;  // 1 KB loads per wave and tile
-  static_assert(kIpw >= 1 && kIpw * kNW * 1024 == kTileB, "tile must split over the waves");
+  static constexpr int kIpw = kTileB / 1024 / NW;   // 1 KB loads per wave and tile
+  static_assert(kIpw >= 1 && kIpw * NW * 1024 == kTileB, "tile must split over the waves");
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
     else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
 };
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
+// NW waves of 32 queries per workgroup; with 4, two workgroups share a CU.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dq_kernel(BwdParams p) {
   using T = BT<D>;
-  using Q = DqDma<D>;
+  using Q = DqDma<D, NW>;
+  constexpr int kUnit = NW * 32;        // queries per unit
+  constexpr int kThreads = NW * 64;
   constexpr int CPR = Q::CPR, RowB = Q::RowB, KTB = Q::kTileB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // K buffer b at b * KTB, V buffer b at (2 + b) * KTB, then the table
@@ -339,10 +357,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams p) {
 // loaded straight into LDS (the dQ kernel's row swizzle); Q rows and dO rows
 // are read as MFMA operands, and dO^T (pass 0) and Q^T (pass 1) with the
 // transposing LDS read.
-template <int D, bool MEM, int PASS>
+template <int D, bool MEM, int PASS, int NW>
 __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   using T = BT<D>;
-  using Q = DqDma<D>;
+  using Q = DqDma<D, NW>;
+  constexpr int kUnit = NW * 32;               // keys per unit
+  constexpr int kThreads = NW * 64;
   constexpr int CPR = Q::CPR, RowB = Q::RowB, TB = Q::kTileB;
   constexpr int kQ = Q::kKeys;                 // queries per iteration
   constexpr int kBufB = 2 * TB + 2 * kQ * 4;   // Q tile, dO tile, lse and Dv
@@ -557,10 +577,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
 // Both passes in one grid: workgroups [0, split) run pass 0 (dV), the rest
 // pass 1 (dK); split is a multiple of 8.  One launch lets the second pass
 // fill the CUs the first leaves idle at its end.
-template <int D, bool MEM>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p, int split) {
-  if ((int)blockIdx.x < split) dkdv_body<D, MEM, 0>(p, blockIdx.x);
-  else dkdv_body<D, MEM, 1>(p, blockIdx.x - split);
+// NW waves of 32 keys per workgroup; with 4, two workgroups share a CU.
+template <int D, bool MEM, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dkdv_kernel(BwdParams p, int split) {
+  if ((int)blockIdx.x < split) dkdv_body<D, MEM, 0, NW>(p, blockIdx.x);
+  else dkdv_body<D, MEM, 1, NW>(p, blockIdx.x - split);
 }
 
 // ---------------------------------------------------------------- memsum
@@ -591,15 +612,16 @@ int set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MEM>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
-  const size_t lds = 2 * (2 * (size_t)DqDma<D>::kTileB + 2 * 64 * 4) + (MEM ? 0 : (size_t)p.m * 4);
+  constexpr int NW = MEM ? BASA_BWD_DKDV_MEM_WAVES : BASA_BWD_DKDV_WAVES, U = NW * 32;
+  const size_t lds = 2 * (2 * (size_t)DqDma<D, NW>::kTileB + 2 * 64 * 4) + (MEM ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
-  const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + kUnit - 1) / kUnit) * p.nqc
-                            : (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
+  const int64_t units = MEM ? (int64_t)p.batch_heads * ((p.G + U - 1) / U) * p.nqc
+                            : (int64_t)p.batch_heads * p.nW * ((p.m + U - 1) / U);
   if (units > INT32_MAX / 4) return BASA_ERR_UNSUPPORTED;
-  if (set_lds(&bwd_dkdv_kernel<D, MEM>, lds)) return BASA_ERR_HIP;
+  if (set_lds(&bwd_dkdv_kernel<D, MEM, NW>, lds)) return BASA_ERR_HIP;
   const int64_t per_pass = 8 * ((units + 7) / 8);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MEM>), dim3((unsigned)(2 * per_pass)), dim3(kThreads), lds,
-                     stream, p, (int)per_pass);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MEM, NW>), dim3((unsigned)(2 * per_pass)), dim3(NW * 64),
+                     lds, stream, p, (int)per_pass);
   return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
@@ -623,12 +645,13 @@ int launch_d(const BwdParams& p, hipStream_t stream) {
   }
   if ((rc = launch_dkdv<D, false>(p, stream))) return rc;
   {
-    const int64_t units = (int64_t)p.batch_heads * p.nW * ((p.m + kUnit - 1) / kUnit);
+    constexpr int NW = BASA_BWD_DQ_WAVES;
+    const int64_t units = (int64_t)p.batch_heads * p.nW * ((p.m + NW * 32 - 1) / (NW * 32));
     const int64_t upx = (units + 7) / 8;
-    const size_t lds = 4 * (size_t)DqDma<D>::kTileB + (size_t)p.m * 4;
+    const size_t lds = 4 * (size_t)DqDma<D, NW>::kTileB + (size_t)p.m * 4;
     if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
-    if (set_lds(&bwd_dq_kernel<D>, lds)) return BASA_ERR_HIP;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(8 * upx)), dim3(kThreads), lds,
+    if (set_lds(&bwd_dq_kernel<D, NW>, lds)) return BASA_ERR_HIP;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(8 * upx)), dim3(NW * 64), lds,
                        stream, p);
     if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
   }
