@@ -402,7 +402,6 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   const int key = kbase + wave * 32 + l32;
   const bool kvalid = key < nkeys;
   const int kcl = min(key, nkeys - 1);
-
   u32x4 kreg[T::QS], vreg[PASS == 1 ? T::QS : 1];
   {
     const uint16_t* ks = MEM ? p.kmem + (int64_t)bh * p.G * D : p.k + base;
