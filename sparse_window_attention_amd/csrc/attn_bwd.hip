@@ -28,6 +28,9 @@
 //            units cover one chunk of the head's queries each and write fp32
 //            partial sums; window-key units write the final dK, dV of their
 //            tokens, adding the pooled memory gradient of the token's cell.
+//            Windows of 129 to 256 tokens instead take one 8-wave unit per
+//            window that loads all of the window's query tiles into LDS once
+//            and runs both passes over them.
 //   memsum   sums the memory partials and divides by the cell size
 // All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 as operands.  Tiles are loaded straight into LDS row-major;
@@ -57,6 +60,12 @@ constexpr int kBlk = 32;               // rows of one MFMA block: keys (dq), que
 #endif
 #ifndef BASA_BWD_DKDV_MEM_WAVES
 #define BASA_BWD_DKDV_MEM_WAVES 8
+#endif
+// Window keys of windows of more than BASA_BWD_DKDV_WAVES * 32 and at most
+// 256 tokens: one 8-wave workgroup per window with the window's query
+// tiles resident in LDS (both passes in one unit); 0 turns it off.
+#ifndef BASA_BWD_DKDV_RESIDENT
+#define BASA_BWD_DKDV_RESIDENT 1
 #endif
 
 template <int D>
@@ -357,7 +366,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dq_kernel(BwdParams p) {
 // loaded straight into LDS (the dQ kernel's row swizzle); Q rows and dO rows
 // are read as MFMA operands, and dO^T (pass 0) and Q^T (pass 1) with the
 // transposing LDS read.
-template <int D, bool MEM, int PASS, int NW>
+template <int P>
+struct pass_c {
+  static constexpr int value = P;
+};
+
+// RES: a window-key unit holding all of its window's keys (m <= NW * 32)
+// loads every query tile of the window (Q, dO, lse, Dv) into LDS once, then
+// runs pass 0 and pass 1 over the resident tiles with no loads or barriers
+// in the loop.  Otherwise the unit runs pass PASS with two tile buffers in
+// turn, loading the next query tile during each iteration.
+template <int D, bool MEM, int PASS, int NW, bool RES = false>
 __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   using T = BT<D>;
   using Q = DqDma<D, NW>;
@@ -366,6 +385,8 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   constexpr int CPR = Q::CPR, RowB = Q::RowB, TB = Q::kTileB;
   constexpr int kQ = Q::kKeys;                 // queries per iteration
   constexpr int kBufB = 2 * TB + 2 * kQ * 4;   // Q tile, dO tile, lse and Dv
+  constexpr int kNB = RES ? kUnit / kQ : 2;    // tile buffers
+  static_assert(!(RES && MEM), "resident query tiles are for window keys");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int bh, kbase, nq, qbase = 0, win = 0;
   if constexpr (MEM) {
@@ -392,17 +413,20 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
   const uint32_t stb = (uint32_t)p.stride_tok * 2u;
   const int nkeys = MEM ? p.G : p.m;
-  int32_t* tab = reinterpret_cast<int32_t*>(smem + 2 * kBufB);
+  int32_t* tab = reinterpret_cast<int32_t*>(smem + kNB * kBufB);
   if constexpr (!MEM) {
     for (int r = tid; r < p.m; r += kThreads) tab[r] = window_token(p.geo, win, r);
     __syncthreads();
   }
+  auto buf = [&](int it) __attribute__((always_inline)) {
+    return smem + (RES ? it : (it & 1)) * kBufB;
+  };
 
   // this lane's key: K (and V) rows as B operands
   const int key = kbase + wave * 32 + l32;
   const bool kvalid = key < nkeys;
   const int kcl = min(key, nkeys - 1);
-  u32x4 kreg[T::QS], vreg[PASS == 1 ? T::QS : 1];
+  u32x4 kreg[T::QS], vreg[(PASS == 1 || RES) ? T::QS : 1];
   {
     const uint16_t* ks = MEM ? p.kmem + (int64_t)bh * p.G * D : p.k + base;
     const uint16_t* vs = MEM ? p.vmem + (int64_t)bh * p.G * D : p.v + base;
@@ -411,13 +435,9 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
 #pragma unroll
     for (int s = 0; s < T::QS; ++s) {
       kreg[s] = buf_load16(rk, koff + hf * D + s * 16, 0);
-      if constexpr (PASS == 1) vreg[s] = buf_load16(rv, koff + hf * D + s * 16, 0);
+      if constexpr (PASS == 1 || RES) vreg[s] = buf_load16(rv, koff + hf * D + s * 16, 0);
     }
   }
-  f32x16 acc[T::DB];
-#pragma unroll
-  for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
-
   const int nit = (nq + kQ - 1) / kQ;
   auto token_of = [&](int q) __attribute__((always_inline)) {
     return MEM ? qbase + q : tab[q];
@@ -427,7 +447,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   // this wave's share of the Q and dO tile loads of iteration it; lse and Dv
   // of the iteration's queries into registers (stored by `put`)
   auto get = [&](int it) __attribute__((always_inline)) {
-    unsigned char* b = smem + (it & 1) * kBufB;
+    unsigned char* b = buf(it);
     // all row tokens first (one LDS wait for the window table), then the loads
     int tok[Q::kIpw];
 #pragma unroll
@@ -457,13 +477,34 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   };
   auto put = [&](int it) __attribute__((always_inline)) {
     if (tid < kQ) {
-      float* sl = reinterpret_cast<float*>(smem + (it & 1) * kBufB + 2 * TB);
+      float* sl = reinterpret_cast<float*>(buf(it) + 2 * TB);
       sl[(tid / kBlk) * 64 + perm32(tid % kBlk)] = lx;
       sl[(tid / kBlk) * 64 + 32 + perm32(tid % kBlk)] = dvx;
     }
   };
-  get(0);
-  put(0);
+  if constexpr (RES) {
+    // every tile's loads first, then the stores of lse and Dv (each waits
+    // for its own global loads, so storing between the tile loads would
+    // hold back the next tile's issue)
+    float lxs[kNB], dvs[kNB];
+#pragma unroll
+    for (int it = 0; it < kNB; ++it)
+      if (it < nit) {
+        get(it);
+        lxs[it] = lx;
+        dvs[it] = dvx;
+      }
+#pragma unroll
+    for (int it = 0; it < kNB; ++it)
+      if (it < nit) {
+        lx = lxs[it];
+        dvx = dvs[it];
+        put(it);
+      }
+  } else {
+    get(0);
+    put(0);
+  }
   // window keys: the pooled-memory cell of the key's token, whose gradient
   // the epilogue adds; its divisions run while the unit's first loads are
   // in flight, off the epilogue's path
@@ -483,55 +524,88 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   const int x = Q::swz(l32);
   const int sq = (lane & 15) >> 2;
   const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
-  for (int it = 0; it < nit; ++it) {
-    if (it + 1 < nit) get(it + 1);
-    const unsigned char* sqt = smem + (it & 1) * kBufB;   // Q tile
-    const unsigned char* sdo = sqt + TB;                  // dO tile
+  auto run = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int PS = decltype(pc)::value;
+    f32x16 acc[T::DB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float* sl = reinterpret_cast<const float*>(sqt + 2 * TB) + kb * 64;
-      f32x16 s{};
+    for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
+    for (int it = 0; it < nit; ++it) {
+      if (!RES && it + 1 < nit) get(it + 1);
+      const unsigned char* sqt = buf(it);                   // Q tile
+      const unsigned char* sdo = sqt + TB;                  // dO tile
+      const float* sl = reinterpret_cast<const float*>(sqt + 2 * TB);   // lse, Dv
+      // The products of query blocks KB0 .. KB0 + NKB - 1 (32 queries each).
+      // With NKB = 2 the accumulation chains of the two blocks are
+      // interleaved and every LDS operand is read two products before its
+      // MFMA (resident tiles: the registers the loads of the unit's next
+      // tiles would take are free); with NKB = 1 each operand is read right
+      // before its MFMA.  Each accumulator sums its terms in the same order
+      // either way.
+      auto blocks = [&](auto kb0c, auto nkbc) __attribute__((always_inline)) {
+        constexpr int KB0 = decltype(kb0c)::value, NKB = decltype(nkbc)::value;
+        constexpr int AH = NKB == 2 ? 2 : 0;   // operand reads ahead
+        // S = Q K^T (t = Q tile, b = K rows) or dP = dO V^T (t = dO tile, b = V rows)
+        auto rowprod = [&](const unsigned char* t, const u32x4 (&b)[T::QS], f32x16 (&o)[NKB])
+            __attribute__((always_inline)) {
+          u32x4 a[AH + 1][NKB];
+          auto rd = [&](int ss) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ss = 0; ss < T::QS; ++ss) {
-        const int off = (kb * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16);
-        s = mfma(*reinterpret_cast<const u32x4*>(sqt + off), kreg[ss], s);
-      }
-      float pr[16];
+            for (int j = 0; j < NKB; ++j)
+              a[ss % (AH + 1)][j] = *reinterpret_cast<const u32x4*>(
+                  t + ((KB0 + j) * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16));
+          };
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + hf * 16 + r4 * 4);
+          for (int ss = 0; ss < AH; ++ss) rd(ss);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pr[4 * r4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + i], c1, -l4[i]));
-      }
-      float w[16];   // pass 0: P; pass 1: dS
-      if constexpr (PASS == 0) {
+          for (int ss = 0; ss < T::QS; ++ss) {
+            if (ss + AH < T::QS) rd(ss + AH);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = pr[i];
-      } else {
-        f32x16 dp{};
+            for (int j = 0; j < NKB; ++j)
+              o[j] = mfma(a[ss % (AH + 1)][j], b[ss], ss == 0 ? f32x16{} : o[j]);
+          }
+        };
+        f32x16 sc[NKB];
+        rowprod(sqt, kreg, sc);
+        float w[NKB][16];   // P, then (pass 1) dS
 #pragma unroll
-        for (int ss = 0; ss < T::QS; ++ss) {
-          const int off = (kb * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16);
-          dp = mfma(*reinterpret_cast<const u32x4*>(sdo + off), vreg[ss], dp);
+        for (int j = 0; j < NKB; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 l4 =
+                *reinterpret_cast<const f32x4*>(sl + (KB0 + j) * 64 + hf * 16 + r4 * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[j][4 * r4 + i] =
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][4 * r4 + i], c1, -l4[i]));
+          }
+        if constexpr (PS == 1) {
+          f32x16 dp[NKB];
+          rowprod(sdo, vreg, dp);
+#pragma unroll
+          for (int j = 0; j < NKB; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 d4 =
+                  *reinterpret_cast<const f32x4*>(sl + (KB0 + j) * 64 + 32 + hf * 16 + r4 * 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) w[j][4 * r4 + i] *= dp[j][4 * r4 + i] - d4[i];
+            }
         }
+        // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS -- the transposed
+        // operand by transposing reads of the row-major tile.  Product i is
+        // (key slice i / DB of these blocks, d block i % DB), so consecutive
+        // products update different accumulators.
+        const unsigned char* tt = PS == 0 ? sdo : sqt;
+        u32x4 pb[2 * NKB];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + hf * 16 + r4 * 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[4 * r4 + i] = pr[4 * r4 + i] * (dp[4 * r4 + i] - d4[i]);
+        for (int u = 0; u < 2 * NKB; ++u) {
+          const float* v = w[u >> 1] + 8 * (u & 1);
+          pb[u] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
         }
-      }
-      // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS -- the transposed
-      // operand by transposing reads of the row-major tile
-      const unsigned char* tt = PASS == 0 ? sdo : sqt;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pb{pack_bf16x2(w[8 * u], w[8 * u + 1]), pack_bf16x2(w[8 * u + 2], w[8 * u + 3]),
-                       pack_bf16x2(w[8 * u + 4], w[8 * u + 5]), pack_bf16x2(w[8 * u + 6], w[8 * u + 7])};
-        const int slc = 2 * kb + u;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
+        constexpr int NP = 2 * NKB * T::DB;
+        auto rdt = [&](int i) __attribute__((always_inline)) {
+          const int slc = 2 * KB0 + i / T::DB, db = i % T::DB;
           bf16x4 h2[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -540,36 +614,56 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
             h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
                 tt + row * RowB + (((d >> 3) ^ Q::swz(row)) * 16) + (d & 7) * 2));
           }
-          const bf16x8 av = {h2[0][0], h2[0][1], h2[0][2], h2[0][3],
-                             h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, pb),
-                                                           acc[db], 0, 0, 0);
+          return bf16x8{h2[0][0], h2[0][1], h2[0][2], h2[0][3], h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+        };
+        bf16x8 av[AH + 1];
+#pragma unroll
+        for (int i = 0; i < AH; ++i) av[i] = rdt(i);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          if (i + AH < NP) av[(i + AH) % (AH + 1)] = rdt(i + AH);
+          acc[i % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              av[i % (AH + 1)], __builtin_bit_cast(bf16x8, pb[i / T::DB]), acc[i % T::DB], 0, 0, 0);
         }
+      };
+      if constexpr (RES) {
+        blocks(pass_c<0>{}, pass_c<2>{});
+      } else {
+        blocks(pass_c<0>{}, pass_c<1>{});
+        blocks(pass_c<1>{}, pass_c<1>{});
+      }
+      if constexpr (!RES) {
+        if (it + 1 < nit) put(it + 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next tiles
+        __syncthreads();
       }
     }
-    if (it + 1 < nit) put(it + 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next tiles
-    __syncthreads();
-  }
 
-  if constexpr (MEM) {
-    // fp32 partials [bh][qc][key][d]; lane = key, registers = 4 consecutive d
-    if (kvalid) {
-      const int qc = qbase / p.qchunk;
-      float* dst = (PASS == 0 ? p.pv : p.pk) + (((int64_t)bh * p.nqc + qc) * p.G + key) * D;
+    if constexpr (MEM) {
+      // fp32 partials [bh][qc][key][d]; lane = key, registers = 4 consecutive d
+      if (kvalid) {
+        const int qc = qbase / p.qchunk;
+        float* dst = (PS == 0 ? p.pv : p.pk) + (((int64_t)bh * p.nqc + qc) * p.G + key) * D;
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db)
+        for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * g + 4 * hf) =
-              f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * g + 4 * hf) =
+                f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      }
+    } else {
+      const int tok = tab[kcl];
+      const float* add = nullptr;
+      if (p.G > 0) add = (PS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
+      store_rows<D>(acc, PS == 0 ? 1.0f : p.scale, add, (PS == 0 ? p.dv : p.dk) + base,
+                    (uint32_t)tok * stb, kvalid, hf);
     }
+  };
+  if constexpr (RES) {
+    run(pass_c<0>{});
+    run(pass_c<1>{});
   } else {
-    const int tok = tab[kcl];
-    const float* add = nullptr;
-    if (p.G > 0) add = (PASS == 0 ? p.gv : p.gk) + ((int64_t)bh * p.G + cell) * D;
-    store_rows<D>(acc, PASS == 0 ? 1.0f : p.scale, add, (PASS == 0 ? p.dv : p.dk) + base,
-                  (uint32_t)tok * stb, kvalid, hf);
+    run(pass_c<PASS>{});
   }
 }
 
@@ -581,6 +675,12 @@ template <int D, bool MEM, int NW>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dkdv_kernel(BwdParams p, int split) {
   if ((int)blockIdx.x < split) dkdv_body<D, MEM, 0, NW>(p, blockIdx.x);
   else dkdv_body<D, MEM, 1, NW>(p, blockIdx.x - split);
+}
+
+// One window per workgroup (m <= 256), both passes over resident query tiles.
+template <int D>
+__global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_res_kernel(BwdParams p) {
+  dkdv_body<D, false, 0, kNW, true>(p, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- memsum
@@ -611,6 +711,19 @@ int set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MEM>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
+  if constexpr (!MEM && BASA_BWD_DKDV_RESIDENT) {
+    if (p.m > BASA_BWD_DKDV_WAVES * 32 && p.m <= kNW * 32) {
+      constexpr int kNB = kNW * 32 / DqDma<D, kNW>::kKeys;
+      const size_t lds = kNB * (2 * (size_t)DqDma<D, kNW>::kTileB + 2 * 64 * 4) + (size_t)p.m * 4;
+      if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
+      const int64_t units = (int64_t)p.batch_heads * p.nW;
+      if (units > INT32_MAX / 4) return BASA_ERR_UNSUPPORTED;
+      if (set_lds(&bwd_dkdv_res_kernel<D>, lds)) return BASA_ERR_HIP;
+      hipLaunchKernelGGL((bwd_dkdv_res_kernel<D>), dim3((unsigned)(8 * ((units + 7) / 8))),
+                         dim3(kNW * 64), lds, stream, p);
+      return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+    }
+  }
   constexpr int NW = MEM ? BASA_BWD_DKDV_MEM_WAVES : BASA_BWD_DKDV_WAVES, U = NW * 32;
   const size_t lds = 2 * (2 * (size_t)DqDma<D, NW>::kTileB + 2 * 64 * 4) + (MEM ? 0 : (size_t)p.m * 4);
   if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
