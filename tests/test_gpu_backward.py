@@ -58,6 +58,9 @@ CASES = [
     # and 256 tokens too): head dim 64, BNHD, a ragged last query tile
     ("head dim 64, window 192, bnhd", 1, 3, 64, (24, 32), (12, 16), (5, 7), (4, 4),
      math.log(16.0), "bnhd"),
+    # the smallest window of that kernel: 129 tokens, the last query tile
+    # holding one row
+    ("window 129", 1, 2, 128, (6, 86), (3, 43), (1, 20), (3, 2), 0.0, "bhnd"),
 ]
 
 
