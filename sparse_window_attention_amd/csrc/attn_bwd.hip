@@ -535,12 +535,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
       const unsigned char* sdo = sqt + TB;                  // dO tile
       const float* sl = reinterpret_cast<const float*>(sqt + 2 * TB);   // lse, Dv
       // The products of query blocks KB0 .. KB0 + NKB - 1 (32 queries each).
-      // With NKB = 2 the accumulation chains of the two blocks are
-      // interleaved and every LDS operand is read two products before its
-      // MFMA (resident tiles: the registers the loads of the unit's next
-      // tiles would take are free); with NKB = 1 each operand is read right
-      // before its MFMA.  Each accumulator sums its terms in the same order
-      // either way.
+      // With NKB = 2 (resident tiles only: the two-buffer kernels spill
+      // with it) the accumulation chains of the two blocks are interleaved
+      // and every LDS operand is read two products before its MFMA; with
+      // NKB = 1 each operand is read right before its MFMA.  Each
+      // accumulator sums its terms in the same order either way.
       auto blocks = [&](auto kb0c, auto nkbc) __attribute__((always_inline)) {
         constexpr int KB0 = decltype(kb0c)::value, NKB = decltype(nkbc)::value;
         constexpr int AH = NKB == 2 ? 2 : 0;   // operand reads ahead
