@@ -49,6 +49,10 @@ namespace {
 
 constexpr float kRescaleSlack = 8.0f; // log2 units the stale max may lag
 constexpr int kStoreNT = 2;            // cache policy of buffer stores: non-temporal
+// Cache policy of the loads of data read once per unit (its Q rows, its
+// window's K and V tiles): non-temporal, leaving the caches to the memory
+// keys, which every unit of the head reads again.
+constexpr int kLoadOnce = 2;
 constexpr int kPersistentMinTiles = 4;  // tiles per unit the persistent kernel needs
 // Persistent kernel: LDS operand reads this many MFMA steps ahead (score
 // product, P V product).
@@ -361,7 +365,7 @@ struct Core {
       const Rsrc rs = make_rsrc((isv ? p.v : p.k) + kvb(u));
 #pragma unroll
       for (int i = 0; i < kDmaIpw; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16, off[i] + cb[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds(i), 16, off[i] + cb[i], 0, 0, kLoadOnce);
     } else if (k0 >= m && k0 + kKT <= L) {
       const Rsrc rs = make_rsrc((isv ? p.vmem : p.kmem) + (int64_t)u.bh * p.G * D);
 #pragma unroll
@@ -959,7 +963,7 @@ __global__ void __launch_bounds__(NW * 64, BASA_PERSISTENT_WGS) attn_bf16_persis
     const char* src = reinterpret_cast<const char*>(p.q + u.base) + c.tok(tb, row) + ch * 16;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                       (__attribute__((address_space(3))) void*)(qstage + i * 1024),
-                                      16, 0, 0);
+                                      16, 0, kLoadOnce);
   };
   auto unstage_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
