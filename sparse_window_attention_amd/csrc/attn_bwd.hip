@@ -28,9 +28,9 @@
 //            units cover one chunk of the head's queries each and write fp32
 //            partial sums; window-key units write the final dK, dV of their
 //            tokens, adding the pooled memory gradient of the token's cell.
-//            Windows of 129 to 256 tokens instead take one 8-wave unit per
-//            window that loads all of the window's query tiles into LDS once
-//            and runs both passes over them.
+//            Windows of 129 to 256 tokens at head dim 128 instead take one
+//            8-wave unit per window that loads all of the window's query
+//            tiles into LDS once and runs both passes over them.
 //   memsum   sums the memory partials and divides by the cell size
 // All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 as operands.  Tiles are loaded straight into LDS row-major;
@@ -62,8 +62,9 @@ constexpr int kBlk = 32;               // rows of one MFMA block: keys (dq), que
 #define BASA_BWD_DKDV_MEM_WAVES 8
 #endif
 // Window keys of windows of more than BASA_BWD_DKDV_WAVES * 32 and at most
-// 256 tokens: one 8-wave workgroup per window with the window's query
-// tiles resident in LDS (both passes in one unit); 0 turns it off.
+// 256 tokens, head dim 128: one 8-wave workgroup per window with the
+// window's query tiles resident in LDS (both passes in one unit); 0 turns
+// it off.  (At head dim 64 the two-buffer kernel measured faster.)
 #ifndef BASA_BWD_DKDV_RESIDENT
 #define BASA_BWD_DKDV_RESIDENT 1
 #endif
@@ -710,7 +711,7 @@ int set_lds(K kernel, size_t bytes) {
 
 template <int D, bool MEM>
 int launch_dkdv(const BwdParams& p, hipStream_t stream) {
-  if constexpr (!MEM && BASA_BWD_DKDV_RESIDENT) {
+  if constexpr (!MEM && BASA_BWD_DKDV_RESIDENT && D == 128) {
     if (p.m > BASA_BWD_DKDV_WAVES * 32 && p.m <= kNW * 32) {
       constexpr int kNB = kNW * 32 / DqDma<D, kNW>::kKeys;
       const size_t lds = kNB * (2 * (size_t)DqDma<D, kNW>::kTileB + 2 * 64 * 4) + (size_t)p.m * 4;

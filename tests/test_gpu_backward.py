@@ -53,13 +53,14 @@ CASES = [
     # the persistent forward with memory-only tiles taking the bias as an offset
     ("memory-only tiles, bias", 1, 2, 128, (64, 64), (16, 16), (8, 3), (4, 4),
      math.log(16.0), "bhnd"),
-    # windows of 129 to 256 tokens take the window-key dK/dV kernel with the
-    # window's query tiles resident in LDS (the cases above with 195, 240
-    # and 256 tokens too): head dim 64, BNHD, a ragged last query tile
+    # head dim 64, BNHD, a window of 129 to 256 tokens with a ragged last
+    # query tile (the two-buffer window-key dK/dV kernel; at head dim 128
+    # such windows take the kernel with the window's query tiles resident in
+    # LDS: the cases above with 195, 240 and 256 tokens)
     ("head dim 64, window 192, bnhd", 1, 3, 64, (24, 32), (12, 16), (5, 7), (4, 4),
      math.log(16.0), "bnhd"),
-    # the smallest window of that kernel: 129 tokens, the last query tile
-    # holding one row
+    # the smallest window of the resident kernel: 129 tokens, the last query
+    # tile holding one row
     ("window 129", 1, 2, 128, (6, 86), (3, 43), (1, 20), (3, 2), 0.0, "bhnd"),
 ]
 
