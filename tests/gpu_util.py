@@ -85,3 +85,31 @@ def make_full_inputs(wl, exact_heads, variant=0):
 def sample_windows(nW, k=4):
     picks = sorted({0, nW - 1, nW // 2, (nW * 3) // 7})
     return picks[:k] if len(picks) > k else picks
+
+
+def random_geometry(seed, f32=True):
+    """A seeded geometry within the API's contract: the window and the pool
+    divide the grid on every axis, shifts anywhere (negative, past the
+    window, past the grid), windows of up to 768 tokens (several query
+    units per window past 256); bf16 only when ``f32`` is false."""
+    rng = np.random.default_rng(seed)
+    nd = int(rng.integers(2, 4))
+    if nd == 2:
+        window = (1024, 1)
+        while window[0] * window[1] > 768:
+            window = (int(rng.integers(2, 29)), int(rng.integers(2, 29)))
+    else:
+        window = (int(rng.integers(1, 5)), int(rng.integers(2, 9)), int(rng.integers(2, 13)))
+    counts = tuple(int(rng.integers(1, 4)) for _ in window)
+    grid = tuple(w * c for w, c in zip(window, counts))
+    shift = tuple(int(rng.integers(-2 * w, 2 * w + 1)) for w in window)
+    pool = None
+    if rng.random() < 0.75:
+        divs = [[d for d in range(1, g + 1) if g % d == 0] for g in grid]
+        pool = tuple(int(rng.choice(d)) for d in divs)
+    D = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.75 or not f32 else "f32"
+    layout = "bhnd" if rng.random() < 0.5 else "bnhd"
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    bias = float(np.log(np.prod(pool))) if pool is not None and rng.random() < 0.5 else 0.0
+    return grid, window, shift, pool, D, dtype, layout, B, H, bias

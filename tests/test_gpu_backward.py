@@ -15,7 +15,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import bhnd_to_bnhd, log, make_full_inputs, random_qkv, to_gpu, to_np
+from gpu_util import bhnd_to_bnhd, log, make_full_inputs, random_geometry, random_qkv, to_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -67,11 +67,25 @@ CASES = [
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_backward_parity(case):
-    name, B, H, D, grid, window, shift, pool, bias, layout = CASES[case]
+    _check_backward(*CASES[case], seeds=(500 + case, 600 + case))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_backward_random_geometries(seed):
+    """Seeded random geometries (bf16): 2D and 3D, windows of up to 768
+    tokens, any shift, with or without a pool and a memory bias, both
+    layouts, head dim 64 or 128."""
+    grid, window, shift, pool, D, _, layout, B, H, bias = random_geometry(3000 + seed, f32=False)
+    _check_backward(f"random {seed} shift={shift}", B, H, D, grid, window, shift, pool, bias,
+                    layout, seeds=(4000 + seed, 5000 + seed))
+
+
+def _check_backward(name, B, H, D, grid, window, shift, pool, bias, layout, seeds):
     n = int(np.prod(grid))
-    log(f"backward '{name}': B={B} H={H} D={D} grid={grid} window={window} pool={pool}")
-    q, k, v = random_qkv((B, H, n, D), "bf16", seed=500 + case)
-    (do,) = random_qkv((B, H, n, D), "bf16", seed=600 + case)[:1]
+    log(f"backward '{name}': B={B} H={H} D={D} grid={grid} window={window} pool={pool} "
+        f"bias={bias:.3f} {layout}")
+    q, k, v = random_qkv((B, H, n, D), "bf16", seed=seeds[0])
+    (do,) = random_qkv((B, H, n, D), "bf16", seed=seeds[1])[:1]
     ref = O.window_attention_backward(q, k, v, do, grid, window, shift, pool,
                                       mem_logit_bias=bias)
     conv = bhnd_to_bnhd if layout == "bnhd" else (lambda x: x)

@@ -10,8 +10,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import (assert_close, bhnd_to_bnhd, log, make_full_inputs, random_qkv, to_gpu,
-                      to_np)
+from gpu_util import (assert_close, bhnd_to_bnhd, log, make_full_inputs, random_geometry,
+                      random_qkv, to_gpu, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,37 +68,9 @@ def test_small_geometries(case, D, dtype):
     assert_close(to_np(out), ref, dtype, f"small {case} D{D} {dtype}")
 
 
-def _random_geometry(seed):
-    """A seeded geometry within the API's contract: the window and the pool
-    divide the grid on every axis, shifts anywhere (negative, past the
-    window, past the grid), windows of up to 768 tokens (several query
-    units per window past 256)."""
-    rng = np.random.default_rng(seed)
-    nd = int(rng.integers(2, 4))
-    if nd == 2:
-        window = (1024, 1)
-        while window[0] * window[1] > 768:
-            window = (int(rng.integers(2, 29)), int(rng.integers(2, 29)))
-    else:
-        window = (int(rng.integers(1, 5)), int(rng.integers(2, 9)), int(rng.integers(2, 13)))
-    counts = tuple(int(rng.integers(1, 4)) for _ in window)
-    grid = tuple(w * c for w, c in zip(window, counts))
-    shift = tuple(int(rng.integers(-2 * w, 2 * w + 1)) for w in window)
-    pool = None
-    if rng.random() < 0.75:
-        divs = [[d for d in range(1, g + 1) if g % d == 0] for g in grid]
-        pool = tuple(int(rng.choice(d)) for d in divs)
-    D = int(rng.choice([64, 128]))
-    dtype = "bf16" if rng.random() < 0.75 else "f32"
-    layout = "bhnd" if rng.random() < 0.5 else "bnhd"
-    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
-    bias = float(np.log(np.prod(pool))) if pool is not None and rng.random() < 0.5 else 0.0
-    return grid, window, shift, pool, D, dtype, layout, B, H, bias
-
-
 @pytest.mark.parametrize("seed", range(24))
 def test_random_geometries(seed):
-    grid, window, shift, pool, D, dtype, layout, B, H, bias = _random_geometry(1000 + seed)
+    grid, window, shift, pool, D, dtype, layout, B, H, bias = random_geometry(1000 + seed)
     n = int(np.prod(grid))
     log(f"random geometry seed={seed} grid={grid} window={window} shift={shift} pool={pool} "
         f"D={D} {dtype} {layout} B={B} H={H} bias={bias:.3f}")
