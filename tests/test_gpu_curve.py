@@ -73,6 +73,44 @@ def test_random_order_ragged(dtype, layout):
     assert_close(got, ref, dtype, f"random order {dtype} {layout}")
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_random_tiles(seed):
+    """Seeded random cases: a random permutation of n tokens, a tile dividing
+    n (up to 768 tokens: several query units per tile past 256), any slide,
+    a random memory row set or none, with or without a bias, both layouts,
+    head dim 64/128, bf16 and fp32."""
+    rng = np.random.default_rng(7000 + seed)
+    tile = int(rng.integers(8, 769))
+    ntiles = int(rng.integers(1, 7))
+    n = tile * ntiles
+    slide = int(rng.integers(-2 * n, 2 * n + 1))
+    G = int(rng.integers(1, min(300, n) + 1)) if rng.random() < 0.7 else 0
+    bias = float(rng.normal()) if G and rng.random() < 0.5 else 0.0
+    D = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    layout = "bhnd" if rng.random() < 0.5 else "bnhd"
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    order = rng.permutation(n)
+    idx = rng.choice(n, G, replace=False) if G else None
+    log(f"random tiles seed={seed} n={n} tile={tile} slide={slide} G={G} bias={bias:.3f} "
+        f"D={D} {dtype} {layout} B={B} H={H}")
+    q, k, v = random_qkv((B, H, n, D), dtype, seed=8000 + seed)
+    km = vm = None
+    if G:
+        km, vm = k[:, :, idx], v[:, :, idx]
+    ref = O.curve_attention(q, k, v, order, tile, slide, km, vm, mem_logit_bias=bias)
+    conv = (lambda x: x) if layout == "bhnd" else bhnd_to_bnhd
+    qg, kg, vg = (to_gpu(conv(x), dtype) for x in (q, k, v))
+    mem = S.gather_kv(kg, vg, _order(idx), layout=layout) if G else None
+    out = S.curve_attn(qg, kg, vg, _order(order), tile, slide, mem=mem, mem_bias=bias,
+                       layout=layout)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    if layout == "bnhd":
+        got = np.transpose(got, (0, 2, 1, 3))
+    assert_close(got, ref, dtype, f"random tiles {seed}")
+
+
 @pytest.mark.parametrize("with_mem", [False, True])
 def test_raster_order_is_row_window_attention(with_mem):
     # the same kernels through both address maps: results agree bit for bit
