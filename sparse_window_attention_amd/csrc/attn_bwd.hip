@@ -232,52 +232,70 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dq_kernel(BwdParams p) {
   const uint16_t* kmem = p.kmem + (int64_t)bh * p.G * D;
   const uint16_t* vmem = p.vmem + (int64_t)bh * p.G * D;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // this wave's share of the loads of iteration it's K and V tiles
+  // this wave's share of the loads of iteration it's K and V tiles; the tile
+  // kind (window rows through the table, memory rows, mixed) and the buffer
+  // resources are decided once per tile
   auto dma = [&](int it) __attribute__((always_inline)) {
     const int k0 = it * Q::kKeys;
     unsigned char* bk = smem + (it & 1) * KTB;
     unsigned char* bv = smem + (2 + (it & 1)) * KTB;
     const bool winT = k0 + Q::kKeys <= p.m;
     const bool memT = k0 >= p.m && k0 + Q::kKeys <= L;
-    // window tiles: all table reads first (one LDS wait), then the loads
-    uint32_t toff[Q::kIpw];
+    int r[Q::kIpw];
+    uint32_t cb[Q::kIpw];
 #pragma unroll
     for (int i = 0; i < Q::kIpw; ++i) {
-      const int r = ((wv * Q::kIpw + i) * 64 + lane) / CPR;
-      toff[i] = winT ? (uint32_t)tab[k0 + r] * stb : 0u;
+      r[i] = ((wv * Q::kIpw + i) * 64 + lane) / CPR;
+      cb[i] = (uint32_t)(((lane % CPR) ^ Q::swz(r[i])) * 16);
     }
+    // LDS destinations of instruction i: bk / bv + (wv * kIpw + i) KB.  Macros,
+    // and offsets named before the builtin calls: with a lambda returning the
+    // LDS pointer, or an offset expression inside the call, the compiler's
+    // host pass silently drops this kernel's launch stub (the library then
+    // fails to load).
+#define BASA_DQ_LK(i) ((__attribute__((address_space(3))) void*)(bk + (wv * Q::kIpw + (i)) * 1024))
+#define BASA_DQ_LV(i) ((__attribute__((address_space(3))) void*)(bv + (wv * Q::kIpw + (i)) * 1024))
+    if (winT) {
+      // all table reads first (one LDS wait), then the loads
+      uint32_t toff[Q::kIpw];
 #pragma unroll
-    for (int i = 0; i < Q::kIpw; ++i) {
-      const int ins = wv * Q::kIpw + i;
-      const int r = (ins * 64 + lane) / CPR;
-      const uint32_t cb = (uint32_t)(((lane % CPR) ^ Q::swz(r)) * 16);
-      auto* lk = (__attribute__((address_space(3))) void*)(bk + ins * 1024);
-      auto* lv = (__attribute__((address_space(3))) void*)(bv + ins * 1024);
-      if (winT) {
-        const uint32_t off = toff[i] + cb;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.k + base), lk, 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.v + base), lv, 16, off, 0, 0, 0);
-      } else if (memT) {
-        const uint32_t off = (uint32_t)(k0 - p.m + r) * (D * 2) + cb;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kmem), lk, 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vmem), lv, 16, off, 0, 0, 0);
-      } else {
-        const int key = min(k0 + r, L - 1);   // rows past the end: clamped, masked below
+      for (int i = 0; i < Q::kIpw; ++i) toff[i] = (uint32_t)tab[k0 + r[i]] * stb;
+      const Rsrc rk = make_rsrc(p.k + base), rvs = make_rsrc(p.v + base);
+#pragma unroll
+      for (int i = 0; i < Q::kIpw; ++i) {
+        const uint32_t off = toff[i] + cb[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, BASA_DQ_LK(i), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, BASA_DQ_LV(i), 16, off, 0, 0, 0);
+      }
+    } else if (memT) {
+      const Rsrc rk = make_rsrc(kmem), rvs = make_rsrc(vmem);
+#pragma unroll
+      for (int i = 0; i < Q::kIpw; ++i) {
+        const uint32_t off = (uint32_t)(k0 - p.m + r[i]) * (D * 2) + cb[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, BASA_DQ_LK(i), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, BASA_DQ_LV(i), 16, off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Q::kIpw; ++i) {
+        const int key = min(k0 + r[i], L - 1);   // rows past the end: clamped, masked below
         const char* gk;
         const char* gvp;
         if (key < p.m) {
-          const int64_t o = (int64_t)tab[key] * stb + cb;
+          const int64_t o = (int64_t)tab[key] * stb + cb[i];
           gk = reinterpret_cast<const char*>(p.k + base) + o;
           gvp = reinterpret_cast<const char*>(p.v + base) + o;
         } else {
-          const int64_t o = (int64_t)(key - p.m) * (D * 2) + cb;
+          const int64_t o = (int64_t)(key - p.m) * (D * 2) + cb[i];
           gk = reinterpret_cast<const char*>(kmem) + o;
           gvp = reinterpret_cast<const char*>(vmem) + o;
         }
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gk, lk, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gvp, lv, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gk, BASA_DQ_LK(i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gvp, BASA_DQ_LV(i), 16, 0, 0);
       }
     }
+#undef BASA_DQ_LK
+#undef BASA_DQ_LV
   };
   dma(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads are in LDS
