@@ -28,9 +28,10 @@
 //            units cover one chunk of the head's queries each and write fp32
 //            partial sums; window-key units write the final dK, dV of their
 //            tokens, adding the pooled memory gradient of the token's cell.
-//            Windows of 129 to 256 tokens at head dim 128 instead take one
-//            8-wave unit per window that loads all of the window's query
-//            tiles into LDS once and runs both passes over them.
+//            Windows of 129 to 256 tokens at head dim 128 instead take
+//            8-wave workgroups, one per CU, each walking windows of its
+//            XCD: a window's query tiles sit in LDS for both passes, and the
+//            next window's tiles are loaded while the dK pass runs.
 //   memsum   sums the memory partials and divides by the cell size
 // All products are 32x32x16 bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 as operands.  Tiles are loaded straight into LDS row-major;
@@ -136,6 +137,57 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[BT<D>::DB], float
       const int d = db * 32 + 8 * (g + 1 - hf);
       if (valid) __builtin_amdgcn_raw_buffer_store_b128(w, rs, off + d * 2, 0, 0);
     }
+}
+
+// store_rows for a kernel that loops over units: the row's byte offset and
+// `add` pass through an empty asm, so that each store and load adds a
+// constant to them in its offset field (rather than the compiler holding
+// every per-lane offset plus constant in a register of its own across the
+// loop), and the `add` values of two d blocks are loaded together, one wait
+// for eight loads.
+template <int D>
+__device__ __forceinline__ void store_rows_u(const f32x16 (&acc)[BT<D>::DB], float mul,
+                                             const float* add, uint16_t* dst_slice,
+                                             uint32_t off, bool valid, int hf) {
+  using gf4 = const __attribute__((address_space(1))) f32x4;
+  const Rsrc rs = make_rsrc(dst_slice);
+  off -= 16 * hf;   // the lane half's part of d
+  asm("" : "+v"(off));
+  const __attribute__((address_space(1))) float* ag = nullptr;
+  if (add != nullptr) {
+    const float* a4 = add + 4 * hf;
+    asm("" : "+v"(a4));
+    ag = (const __attribute__((address_space(1))) float*)a4;
+  }
+#pragma unroll
+  for (int db0 = 0; db0 < BT<D>::DB; db0 += 2) {
+    f32x4 x[2][4] = {};
+    if (ag != nullptr && valid) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) x[u][g] = *(gf4*)(ag + (db0 + u) * 32 + 8 * g);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; g += 2) {
+        const int db = db0 + u;
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = acc[db][4 * g + i] * mul + x[u][g][i];
+          a[4 + i] = acc[db][4 * g + 4 + i] * mul + x[u][g + 1][i];
+        }
+        const uint32_t a0 = pack_bf16x2(a[0], a[1]), a1 = pack_bf16x2(a[2], a[3]);
+        const uint32_t b0 = pack_bf16x2(a[4], a[5]), b1 = pack_bf16x2(a[6], a[7]);
+        const auto x0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+        const u32x4 w{x0[0], x1[0], x0[1], x1[1]};
+        if (valid)
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, off + (db * 32 + 8 * (g + 1)) * 2, 0, 0);
+      }
+  }
 }
 
 // ---------------------------------------------------------------- dvec
@@ -385,6 +437,164 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dq_kernel(BwdParams p) {
 // loaded straight into LDS (the dQ kernel's row swizzle); Q rows and dO rows
 // are read as MFMA operands, and dO^T (pass 0) and Q^T (pass 1) with the
 // transposing LDS read.
+// The products of one query tile (Q rows at sqt, dO rows at sqt + TB, lse
+// and Dv at slp) for its 32-query blocks KB0 .. KB0 + NKB - 1, against
+// this wave's 32 keys (K and V rows in registers), accumulated into acc:
+// pass PS = 0: dV^T += dO^T P; PS = 1: dK^T += Q^T dS.  With NKB = 2 the
+// accumulation chains of the two blocks are interleaved and every LDS
+// operand is read two products before its MFMA; with NKB = 1 each operand
+// is read right before its MFMA.  Each accumulator sums its terms in the
+// same order either way.
+using lds_cu8 = const __attribute__((address_space(3))) unsigned char;
+
+// base + off as an LDS address; with FA, formed in a register the compiler
+// cannot see through (an asm without side effects: loads still move freely
+// around it).  In a loop over LDS buffers each address is then one such sum
+// per iteration, with its constant part in the instruction's offset field;
+// otherwise every (per-lane offset + constant) may be hoisted out of the
+// loop into a register of its own and the buffer base added at each read.
+template <bool FA>
+__device__ __forceinline__ lds_cu8* lds_at(const unsigned char* base, uint32_t off) {
+  uint32_t a = (uint32_t)(uintptr_t)(lds_cu8*)base + off;
+  if constexpr (FA) asm("" : "+v"(a));
+  return (lds_cu8*)(uintptr_t)a;
+}
+
+template <int D, int NW, int PS, int KB0, int NKB, bool FA = false>
+__device__ __forceinline__ void dkdv_blocks(const unsigned char* sqt, const unsigned char* slp,
+                                            const u32x4* kreg,
+                                            const u32x4* vreg, f32x16 (&acc)[BT<D>::DB],
+                                            float c1, int l32, int hf, int lane) {
+  using T = BT<D>;
+  using Q = DqDma<D, NW>;
+  using lds_v4 = const __attribute__((address_space(3))) u32x4;
+  using lds_f4 = const __attribute__((address_space(3))) f32x4;
+  using lds_h4 = __attribute__((address_space(3))) bf16x4;
+  constexpr int CPR = Q::CPR, RowB = Q::RowB, TB = Q::kTileB;
+  const int x = Q::swz(l32);
+  const int sq = (lane & 15) >> 2;
+  const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
+  constexpr int AH = NKB == 2 ? 2 : 0;   // operand reads ahead
+  // With FA, each address is the per-lane part formed on the tile's base
+  // (lds_at) plus a constant (block, row slice, dO tile).
+  // chunk ss of row l32 (S = Q K^T and dP = dO V^T A operands)
+  lds_cu8* ra[T::QS];
+  // lse of this lane's rows (Dv 32 floats further)
+  lds_cu8* rl = nullptr;
+  // transposing reads: row 8h + 4hf + sq of each 16-row slice, d block db
+  // (the swizzle depends on the row modulo 16 only)
+  lds_cu8* rt[2][T::DB];
+  if constexpr (FA) {
+#pragma unroll
+    for (int ss = 0; ss < T::QS; ++ss)
+      ra[ss] = lds_at<FA>(sqt, l32 * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16));
+    rl = lds_at<FA>(slp, hf * 64);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int row = 8 * h + 4 * hf + sq;
+        const int d = 32 * db + d0;
+        rt[h][db] = lds_at<FA>(sqt, row * RowB + (((d >> 3) ^ Q::swz(row)) * 16) + (d & 7) * 2);
+      }
+  }
+  // A operand chunk ss of row l32 of block KB0 + j, tile at toff
+  auto rda = [&](int toff, int ss, int j) __attribute__((always_inline)) {
+    if constexpr (FA) return *(lds_v4*)(ra[ss] + toff + (KB0 + j) * 32 * RowB);
+    else
+      return *reinterpret_cast<const u32x4*>(sqt + toff + ((KB0 + j) * 32 + l32) * RowB +
+                                             (((hf * (CPR / 2) + ss) ^ x) * 16));
+  };
+  // 4 floats of the lse / Dv array at float offset o (+ this lane's rows)
+  auto rdl = [&](int o) __attribute__((always_inline)) {
+    if constexpr (FA) return *(lds_f4*)(rl + o * 4);
+    else return *reinterpret_cast<const f32x4*>(slp + (o + hf * 16) * 4);
+  };
+  // S = Q K^T (tile at toff 0, b = K rows) or dP = dO V^T (toff TB, b = V rows)
+  auto rowprod = [&](int toff, const u32x4* b, f32x16 (&o)[NKB])
+      __attribute__((always_inline)) {
+    u32x4 a[AH + 1][NKB];
+    auto rd = [&](int ss) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < NKB; ++j)
+        a[ss % (AH + 1)][j] = rda(toff, ss, j);
+    };
+#pragma unroll
+    for (int ss = 0; ss < AH; ++ss) rd(ss);
+#pragma unroll
+    for (int ss = 0; ss < T::QS; ++ss) {
+      if (ss + AH < T::QS) rd(ss + AH);
+#pragma unroll
+      for (int j = 0; j < NKB; ++j)
+        o[j] = mfma(a[ss % (AH + 1)][j], b[ss], ss == 0 ? f32x16{} : o[j]);
+    }
+  };
+  f32x16 sc[NKB];
+  rowprod(0, kreg, sc);
+  float w[NKB][16];   // P, then (pass 1) dS
+#pragma unroll
+  for (int j = 0; j < NKB; ++j)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = rdl((KB0 + j) * 64 + r4 * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[j][4 * r4 + i] =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][4 * r4 + i], c1, -l4[i]));
+    }
+  if constexpr (PS == 1) {
+    f32x16 dp[NKB];
+    rowprod(TB, vreg, dp);
+#pragma unroll
+    for (int j = 0; j < NKB; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 d4 = rdl((KB0 + j) * 64 + 32 + r4 * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[j][4 * r4 + i] *= dp[j][4 * r4 + i] - d4[i];
+      }
+  }
+  // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS -- the transposed
+  // operand by transposing reads of the row-major tile.  Product i is
+  // (key slice i / DB of these blocks, d block i % DB), so consecutive
+  // products update different accumulators.
+  constexpr int tto = PS == 0 ? TB : 0;
+  u32x4 pb[2 * NKB];
+#pragma unroll
+  for (int u = 0; u < 2 * NKB; ++u) {
+    const float* v = w[u >> 1] + 8 * (u & 1);
+    pb[u] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+  constexpr int NP = 2 * NKB * T::DB;
+  auto rdt = [&](int i) __attribute__((always_inline)) {
+    const int slc = 2 * KB0 + i / T::DB, db = i % T::DB;
+    bf16x4 h2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (FA) {
+        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_h4*)(rt[h][db] + tto + 16 * slc * RowB));
+      } else {
+        const int row = 16 * slc + 8 * h + 4 * hf + sq;
+        const int d = 32 * db + d0;
+        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_h4*)(
+            sqt + tto + row * RowB + (((d >> 3) ^ Q::swz(row)) * 16) + (d & 7) * 2));
+      }
+    }
+    return bf16x8{h2[0][0], h2[0][1], h2[0][2], h2[0][3], h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
+  };
+  bf16x8 av[AH + 1];
+#pragma unroll
+  for (int i = 0; i < AH; ++i) av[i] = rdt(i);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (i + AH < NP) av[(i + AH) % (AH + 1)] = rdt(i + AH);
+    acc[i % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        av[i % (AH + 1)], __builtin_bit_cast(bf16x8, pb[i / T::DB]), acc[i % T::DB], 0, 0, 0);
+  }
+}
+
 template <int P>
 struct pass_c {
   static constexpr int value = P;
@@ -540,9 +750,6 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads are in LDS
   __syncthreads();
   const float c1 = p.c1;
-  const int x = Q::swz(l32);
-  const int sq = (lane & 15) >> 2;
-  const int d0 = 16 * (l32 >> 4) + 4 * (lane & 3);
   auto run = [&](auto pc) __attribute__((always_inline)) {
     constexpr int PS = decltype(pc)::value;
     f32x16 acc[T::DB];
@@ -550,105 +757,12 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
     for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
     for (int it = 0; it < nit; ++it) {
       if (!RES && it + 1 < nit) get(it + 1);
-      const unsigned char* sqt = buf(it);                   // Q tile
-      const unsigned char* sdo = sqt + TB;                  // dO tile
-      const float* sl = reinterpret_cast<const float*>(sqt + 2 * TB);   // lse, Dv
-      // The products of query blocks KB0 .. KB0 + NKB - 1 (32 queries each).
-      // With NKB = 2 (resident tiles only: the two-buffer kernels spill
-      // with it) the accumulation chains of the two blocks are interleaved
-      // and every LDS operand is read two products before its MFMA; with
-      // NKB = 1 each operand is read right before its MFMA.  Each
-      // accumulator sums its terms in the same order either way.
-      auto blocks = [&](auto kb0c, auto nkbc) __attribute__((always_inline)) {
-        constexpr int KB0 = decltype(kb0c)::value, NKB = decltype(nkbc)::value;
-        constexpr int AH = NKB == 2 ? 2 : 0;   // operand reads ahead
-        // S = Q K^T (t = Q tile, b = K rows) or dP = dO V^T (t = dO tile, b = V rows)
-        auto rowprod = [&](const unsigned char* t, const u32x4 (&b)[T::QS], f32x16 (&o)[NKB])
-            __attribute__((always_inline)) {
-          u32x4 a[AH + 1][NKB];
-          auto rd = [&](int ss) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < NKB; ++j)
-              a[ss % (AH + 1)][j] = *reinterpret_cast<const u32x4*>(
-                  t + ((KB0 + j) * 32 + l32) * RowB + (((hf * (CPR / 2) + ss) ^ x) * 16));
-          };
-#pragma unroll
-          for (int ss = 0; ss < AH; ++ss) rd(ss);
-#pragma unroll
-          for (int ss = 0; ss < T::QS; ++ss) {
-            if (ss + AH < T::QS) rd(ss + AH);
-#pragma unroll
-            for (int j = 0; j < NKB; ++j)
-              o[j] = mfma(a[ss % (AH + 1)][j], b[ss], ss == 0 ? f32x16{} : o[j]);
-          }
-        };
-        f32x16 sc[NKB];
-        rowprod(sqt, kreg, sc);
-        float w[NKB][16];   // P, then (pass 1) dS
-#pragma unroll
-        for (int j = 0; j < NKB; ++j)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 l4 =
-                *reinterpret_cast<const f32x4*>(sl + (KB0 + j) * 64 + hf * 16 + r4 * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              w[j][4 * r4 + i] =
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][4 * r4 + i], c1, -l4[i]));
-          }
-        if constexpr (PS == 1) {
-          f32x16 dp[NKB];
-          rowprod(sdo, vreg, dp);
-#pragma unroll
-          for (int j = 0; j < NKB; ++j)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4 d4 =
-                  *reinterpret_cast<const f32x4*>(sl + (KB0 + j) * 64 + 32 + hf * 16 + r4 * 4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) w[j][4 * r4 + i] *= dp[j][4 * r4 + i] - d4[i];
-            }
-        }
-        // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS -- the transposed
-        // operand by transposing reads of the row-major tile.  Product i is
-        // (key slice i / DB of these blocks, d block i % DB), so consecutive
-        // products update different accumulators.
-        const unsigned char* tt = PS == 0 ? sdo : sqt;
-        u32x4 pb[2 * NKB];
-#pragma unroll
-        for (int u = 0; u < 2 * NKB; ++u) {
-          const float* v = w[u >> 1] + 8 * (u & 1);
-          pb[u] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-        }
-        constexpr int NP = 2 * NKB * T::DB;
-        auto rdt = [&](int i) __attribute__((always_inline)) {
-          const int slc = 2 * KB0 + i / T::DB, db = i % T::DB;
-          bf16x4 h2[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int row = 16 * slc + 8 * h + 4 * hf + sq;
-            const int d = 32 * db + d0;
-            h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(
-                tt + row * RowB + (((d >> 3) ^ Q::swz(row)) * 16) + (d & 7) * 2));
-          }
-          return bf16x8{h2[0][0], h2[0][1], h2[0][2], h2[0][3], h2[1][0], h2[1][1], h2[1][2], h2[1][3]};
-        };
-        bf16x8 av[AH + 1];
-#pragma unroll
-        for (int i = 0; i < AH; ++i) av[i] = rdt(i);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          if (i + AH < NP) av[(i + AH) % (AH + 1)] = rdt(i + AH);
-          acc[i % T::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              av[i % (AH + 1)], __builtin_bit_cast(bf16x8, pb[i / T::DB]), acc[i % T::DB], 0, 0, 0);
-        }
-      };
+      const unsigned char* sqt = buf(it);   // Q tile, dO tile, lse and Dv
       if constexpr (RES) {
-        blocks(pass_c<0>{}, pass_c<2>{});
+        dkdv_blocks<D, NW, PS, 0, 2>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
       } else {
-        blocks(pass_c<0>{}, pass_c<1>{});
-        blocks(pass_c<1>{}, pass_c<1>{});
+        dkdv_blocks<D, NW, PS, 0, 1>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
+        dkdv_blocks<D, NW, PS, 1, 1>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
       }
       if constexpr (!RES) {
         if (it + 1 < nit) put(it + 1);
@@ -695,10 +809,266 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dkdv_kernel(BwdParams p, 
   else dkdv_body<D, MEM, 1, NW>(p, blockIdx.x - split);
 }
 
-// One window per workgroup (m <= 256), both passes over resident query tiles.
+// x, wave-uniform, through an empty asm the compiler cannot see through: the
+// set-up of a division by x (its reciprocal) is then recomputed where the
+// division is, instead of hoisted out of an outer loop and held in registers
+// across it.
+__device__ __forceinline__ int32_t opaque_s(int32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+// The same for a per-lane value: what is computed from it is recomputed
+// where it is used rather than held in registers across a loop.
+__device__ __forceinline__ int32_t opaque_v(int32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Window keys of windows of at most 256 tokens, one 8-wave workgroup per
+// CU walking the (batch, head, window) units of one XCD.  A unit holds all
+// of its window's query tiles (Q, dO) and their lse and Dv in LDS and runs
+// pass 0 (dV) and pass 1 (dK) over them.  The next unit's tiles are loaded
+// while pass 1 runs, tile it into buffer it as soon as every wave is done
+// with it (BASA_BWD_RES_PREFETCH 2: the last wave to finish the tile, told
+// by a count in LDS, issues the whole tile's loads, and no wave waits; 1: a
+// barrier after each tile, then each wave its share; 0: no prefetch, the
+// loads after the unit).  The next unit's K and V rows, lse and Dv are
+// loaded after the dK epilogue.  The window token tables and the lse / Dv
+// arrays alternate between two slots by unit parity.
+#ifndef BASA_BWD_RES_PREFETCH
+#define BASA_BWD_RES_PREFETCH 2
+#endif
+template <int D>
+__device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
+  constexpr int NW = kNW;
+  constexpr int PF = BASA_BWD_RES_PREFETCH;
+  using T = BT<D>;
+  using Q = DqDma<D, NW>;
+  constexpr int kThreads = NW * 64;
+  constexpr int CPR = Q::CPR, TB = Q::kTileB;
+  constexpr int kQ = Q::kKeys;                 // queries per tile
+  constexpr int kMaxM = NW * 32;               // window tokens at most (keys of the unit)
+  constexpr int kNB = kMaxM / kQ;              // tile buffers
+  constexpr int kSlB = 2 * kQ * 4;             // lse and Dv of one tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int units = p.batch_heads * p.nW;
+  const int upx = (units + 7) / 8;
+  const int S = (int)(gridDim.x >> 3);
+  const int ubeg = (int)(blockIdx.x & 7) * upx, uend = min(ubeg + upx, units);
+  const int first = ubeg + (int)(blockIdx.x >> 3);
+  if (first >= uend) return;                   // whole workgroup exits together
+  const int J = (uend - first + S - 1) / S;    // units of this workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t stb = (uint32_t)p.stride_tok * 2u;
+  const int m = p.m;
+  const int nit = (m + kQ - 1) / kQ;
+  const int key = wave * 32 + l32;             // this lane's key of the window
+  const bool kvalid = key < m;
+  const int kcl = min(key, m - 1);
+  const float c1 = p.c1;
+  // LDS: kNB Q/dO tile buffers, two slots of kNB lse/Dv arrays, two table
+  // slots, kNB finish counts
+  auto buf = [&](int it) __attribute__((always_inline)) { return smem + it * (2 * TB); };
+  auto slb = [&](int j, int it) __attribute__((always_inline)) {
+    return smem + kNB * (2 * TB) + ((j & 1) * kNB + it) * kSlB;
+  };
+  auto tab_of = [&](int j) __attribute__((always_inline)) {
+    return reinterpret_cast<int32_t*>(smem + kNB * (2 * TB) + 2 * kNB * kSlB) + (j & 1) * kMaxM;
+  };
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + kNB * (2 * TB) + 2 * kNB * kSlB) + 2 * kMaxM;
+  // unit j's window and (batch, head) slice, wave-uniform (scalar registers:
+  // the buffer resources built from them stay scalar)
+  auto win_of = [&](int j) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane((first + j * S) % opaque_s(p.nW));
+  };
+  auto bh_of = [&](int j) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane((first + j * S) / opaque_s(p.nW));
+  };
+  auto build_table = [&](int32_t* tab, int win) __attribute__((always_inline)) {
+    Geometry g = p.geo;
+    g.nwx = opaque_s(g.nwx);
+    g.nwy = opaque_s(g.nwy);
+    for (int r = tid; r < m; r += kThreads) tab[r] = window_token(g, win, r);
+  };
+  // Q and dO loads of query tile it into buffer it: 1 KB instructions i0,
+  // i0 + 1, ..., i0 + n - 1 of the tile
+  auto tile_part = [&](int it, int i0, int n, int64_t base, const int32_t* tab)
+      __attribute__((always_inline)) {
+    unsigned char* b = buf(it);
+    const int ln = opaque_v(lane);   // addresses computed here, not held across pass 1
+    const Rsrc rq = make_rsrc(p.q + base), rd = make_rsrc(p.dout + base);
+#pragma unroll 1
+    for (int i4 = 0; i4 < n; i4 += 4) {
+      int tok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ((i0 + i4 + i) * 64 + ln) / CPR;
+        tok[i] = (i4 + i < n) ? tab[min(it * kQ + r, m - 1)] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i4 + i < n) {
+          const int ins = i0 + i4 + i;
+          const int r = (ins * 64 + ln) / CPR;
+          const uint32_t off =
+              (uint32_t)tok[i] * stb + (uint32_t)(((ln % CPR) ^ Q::swz(r)) * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq,
+              (__attribute__((address_space(3))) void*)(b + ins * 1024), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rd,
+              (__attribute__((address_space(3))) void*)(b + TB + ins * 1024), 16, off, 0, 0, 0);
+        }
+      }
+    }
+  };
+  // this wave's share of tile it
+  auto tiles = [&](int it, int64_t base, const int32_t* tab) __attribute__((always_inline)) {
+    tile_part(it, wv * Q::kIpw, Q::kIpw, base, tab);
+  };
+  // log2-scale log-sum-exp and Dv of tile it's queries (threads < kQ); a
+  // missing query gets P = 0
+  auto vec = [&](int it, int bh, const int32_t* tab, float& lx, float& dvx)
+      __attribute__((always_inline)) {
+    if (tid < kQ) {
+      const int q = it * kQ + tid;
+      const bool ok = q < m;
+      const int64_t idx = (int64_t)bh * p.n + tab[ok ? q : m - 1];
+      lx = ok ? p.lse[idx] * kLog2e : INFINITY;
+      dvx = ok ? p.dvec[idx] : 0.0f;
+    }
+  };
+  auto put = [&](int j, int it, float lx, float dvx) __attribute__((always_inline)) {
+    if (tid < kQ) {
+      float* sl = reinterpret_cast<float*>(slb(j, it));
+      sl[(tid / kBlk) * 64 + perm32(tid % kBlk)] = lx;
+      sl[(tid / kBlk) * 64 + 32 + perm32(tid % kBlk)] = dvx;
+    }
+  };
+  u32x4 kreg[T::QS], vreg[T::QS];   // this lane's K and V rows (B operands)
+  auto rows = [&](int64_t base, const int32_t* tab) __attribute__((always_inline)) {
+    const uint32_t koff = (uint32_t)tab[kcl] * stb;
+    const Rsrc rk = make_rsrc(p.k + base), rv = make_rsrc(p.v + base);
+#pragma unroll
+    for (int s = 0; s < T::QS; ++s) {
+      kreg[s] = buf_load16(rk, koff + hf * D + s * 16, 0);
+      vreg[s] = buf_load16(rv, koff + hf * D + s * 16, 0);
+    }
+  };
+  // the pooled-memory cell of this lane's key token, whose gradient the
+  // epilogues add
+  auto cell_of = [&](const int32_t* tab) __attribute__((always_inline)) {
+    if (p.G == 0) return 0;
+    const int tok = tab[kcl];
+    const int Wg = opaque_s(p.geo.Wg), Hg = opaque_s(p.geo.Hg);
+    const int xx = tok % Wg;
+    const int y = (tok / Wg) % Hg;
+    const int t = tok / opaque_s(Wg * Hg);
+    return ((t / opaque_s(p.pt)) * p.Gy + y / opaque_s(p.py)) * p.Gx + xx / opaque_s(p.px);
+  };
+
+  // unit 0: its table, rows, tiles, lse and Dv
+  build_table(tab_of(0), win_of(0));
+  if (tid < kNB) cnt[tid] = 0;
+  __syncthreads();
+  float lxs[kNB], dvs[kNB];
+  {
+    const int bh = bh_of(0);
+    const int64_t base = slice_base(p, bh);
+    rows(base, tab_of(0));
+#pragma unroll
+    for (int it = 0; it < kNB; ++it)
+      if (it < nit) tiles(it, base, tab_of(0));
+#pragma unroll
+    for (int it = 0; it < kNB; ++it)
+      if (it < nit) vec(it, bh, tab_of(0), lxs[it], dvs[it]);
+  }
+  for (int j = 0; j < J; ++j) {
+    const bool has_next = j + 1 < J;
+    const int32_t* tab = tab_of(j);
+    const int bh = bh_of(j);
+    const int64_t base = slice_base(p, bh);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the unit have landed
+#pragma unroll
+    for (int it = 0; it < kNB; ++it)
+      if (it < nit) put(j, it, lxs[it], dvs[it]);
+    // Every wave's tiles, lse and Dv are in LDS; every wave is done with the
+    // previous unit (its table and lse / Dv slots are free for the next unit's).
+    __syncthreads();
+    const int bhn = has_next ? bh_of(j + 1) : bh;
+    const int64_t basen = slice_base(p, bhn);
+    if (has_next) build_table(tab_of(j + 1), win_of(j + 1));
+    {  // pass 0: dV
+      f32x16 acc[T::DB];
+#pragma unroll
+      for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
+      for (int it = 0; it < nit; ++it)
+        dkdv_blocks<D, NW, 0, 0, 2, true>(buf(it), slb(j, it), kreg, vreg, acc, c1, l32, hf,
+                                          lane);
+      const float* add = p.G > 0 ? p.gv + ((int64_t)bh * p.G + cell_of(tab)) * D : nullptr;
+      store_rows_u<D>(acc, 1.0f, add, p.dv + base, (uint32_t)tab[kcl] * stb, kvalid, hf);
+    }
+    {  // pass 1: dK; the next unit's tiles go into the buffers it leaves
+      f32x16 acc[T::DB];
+#pragma unroll
+      for (int i = 0; i < T::DB; ++i) acc[i] = f32x16{};
+      bool last_tile = false;   // PF 2: this wave loads the last tile after the epilogue
+      for (int it = 0; it < nit; ++it) {
+        dkdv_blocks<D, NW, 1, 0, 2, true>(buf(it), slb(j, it), kreg, vreg, acc, c1, l32, hf,
+                                          lane);
+        if (PF == 1 && has_next && it + 1 < nit) {
+          __syncthreads();   // every wave is done with buffer it (and the next table is built)
+          tiles(it, basen, tab_of(j + 1));
+        }
+        if (PF == 2 && has_next) {
+          // This wave's reads of buffer it precede the count (LDS operations
+          // of a wave run in order; the empty asm keeps the compiler from
+          // moving them past it).  The wave whose count completes the tile
+          // loads all of it; the next table was built before the unit's
+          // pass 0 by every wave, whose counts it has seen.
+          asm volatile("" ::: "memory");
+          int old = 0;
+          if (lane == 0)
+            old = __hip_atomic_fetch_add(cnt + it, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+          old = __builtin_amdgcn_readfirstlane(old);
+          if (old % NW == NW - 1) {
+            if (it + 1 < nit) tile_part(it, 0, NW * Q::kIpw, basen, tab_of(j + 1));
+            else last_tile = true;
+          }
+        }
+      }
+      // the epilogue's loads wait only for tile loads issued a tile earlier
+      const float* add = p.G > 0 ? p.gk + ((int64_t)bh * p.G + cell_of(tab)) * D : nullptr;
+      store_rows_u<D>(acc, p.scale, add, p.dk + base, (uint32_t)tab[kcl] * stb, kvalid, hf);
+      if (last_tile) tile_part(nit - 1, 0, NW * Q::kIpw, basen, tab_of(j + 1));
+    }
+    if (has_next) {   // the next unit's tiles (without prefetch: all, PF 1: the last), K and
+                      // V rows, lse and Dv
+      if (PF == 0) {
+        __syncthreads();   // every wave is done with the buffers
+#pragma unroll
+        for (int it = 0; it < kNB; ++it)
+          if (it < nit) tiles(it, basen, tab_of(j + 1));
+      }
+      if (PF == 1) {
+        __syncthreads();   // every wave is done with the last buffer
+        tiles(nit - 1, basen, tab_of(j + 1));
+      }
+      rows(basen, tab_of(j + 1));
+#pragma unroll
+      for (int it = 0; it < kNB; ++it)
+        if (it < nit) vec(it, bhn, tab_of(j + 1), lxs[it], dvs[it]);
+    }
+  }
+}
+
+#ifndef BASA_BWD_RES_PERSISTENT
+#define BASA_BWD_RES_PERSISTENT 1
+#endif
 template <int D>
 __global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_res_kernel(BwdParams p) {
-  dkdv_body<D, false, 0, kNW, true>(p, blockIdx.x);
+  if constexpr (BASA_BWD_RES_PERSISTENT) dkdv_res_body<D>(p);
+  else dkdv_body<D, false, 0, kNW, true>(p, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- memsum
@@ -732,12 +1102,21 @@ int launch_dkdv(const BwdParams& p, hipStream_t stream) {
   if constexpr (!MEM && BASA_BWD_DKDV_RESIDENT && D == 128) {
     if (p.m > BASA_BWD_DKDV_WAVES * 32 && p.m <= kNW * 32) {
       constexpr int kNB = kNW * 32 / DqDma<D, kNW>::kKeys;
-      const size_t lds = kNB * (2 * (size_t)DqDma<D, kNW>::kTileB + 2 * 64 * 4) + (size_t)p.m * 4;
+      // tile buffers with their lse / Dv, then one table; persistent: tile
+      // buffers, two slots of lse / Dv arrays and of tables, finish counts
+      const size_t lds = BASA_BWD_RES_PERSISTENT
+          ? kNB * (2 * (size_t)DqDma<D, kNW>::kTileB + 2 * 2 * 64 * 4) + 2 * (size_t)kNW * 32 * 4 +
+                kNB * 4
+          : kNB * (2 * (size_t)DqDma<D, kNW>::kTileB + 2 * 64 * 4) + (size_t)p.m * 4;
       if (lds > 160 * 1024) return BASA_ERR_UNSUPPORTED;
       const int64_t units = (int64_t)p.batch_heads * p.nW;
       if (units > INT32_MAX / 4) return BASA_ERR_UNSUPPORTED;
       if (set_lds(&bwd_dkdv_res_kernel<D>, lds)) return BASA_ERR_HIP;
-      hipLaunchKernelGGL((bwd_dkdv_res_kernel<D>), dim3((unsigned)(8 * ((units + 7) / 8))),
+      // persistent: at most 32 workgroups per XCD (one per CU of an MI355X);
+      // any count is correct, the workgroups share nothing
+      const int64_t upx = (units + 7) / 8;
+      const int64_t per_xcd = BASA_BWD_RES_PERSISTENT ? std::min<int64_t>(upx, 32) : upx;
+      hipLaunchKernelGGL((bwd_dkdv_res_kernel<D>), dim3((unsigned)(8 * per_xcd)),
                          dim3(kNW * 64), lds, stream, p);
       return hipGetLastError() == hipSuccess ? BASA_OK : BASA_ERR_HIP;
     }

@@ -62,6 +62,14 @@ CASES = [
     # the smallest window of the resident kernel: 129 tokens, the last query
     # tile holding one row
     ("window 129", 1, 2, 128, (6, 86), (3, 43), (1, 20), (3, 2), 0.0, "bhnd"),
+    # more (batch, head, window) units than the resident kernel's workgroups
+    # (32 per XCD), so that workgroups walk several units and load the next
+    # unit's query tiles during the current one: 432 units of 169 tokens
+    # (one or two per workgroup, the last query tile of 41 rows) with
+    # memory, and 576 units of 225 tokens (two or three per workgroup)
+    # without memory
+    ("unit walk, window 169", 2, 24, 128, (39, 39), (13, 13), (6, 6), (3, 3), 0.0, "bhnd"),
+    ("unit walk, window 225, bnhd", 1, 64, 128, (45, 45), (15, 15), (7, 3), None, 0.0, "bnhd"),
 ]
 
 
