@@ -834,7 +834,10 @@ __device__ __forceinline__ int32_t opaque_v(int32_t x) {
 // barrier after each tile, then each wave its share; 0: no prefetch, the
 // loads after the unit).  The next unit's K and V rows, lse and Dv are
 // loaded after the dK epilogue.  The window token tables and the lse / Dv
-// arrays alternate between two slots by unit parity.
+// arrays alternate between two slots by unit parity.  Wave w writes and
+// reads rows w*32 .. w*32+31 of each table (its keys, and the same tokens
+// as queries for their lse and Dv); only whole-tile loads read the rows of
+// other waves, after the count or barrier that follows every wave's rows.
 #ifndef BASA_BWD_RES_PREFETCH
 #define BASA_BWD_RES_PREFETCH 2
 #endif
@@ -885,11 +888,12 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
   auto bh_of = [&](int j) __attribute__((always_inline)) {
     return __builtin_amdgcn_readfirstlane((first + j * S) / opaque_s(p.nW));
   };
-  auto build_table = [&](int32_t* tab, int win) __attribute__((always_inline)) {
+  // this wave's rows of a table (kMaxM = 32 rows per wave)
+  auto build_rows = [&](int32_t* tab, int win) __attribute__((always_inline)) {
     Geometry g = p.geo;
     g.nwx = opaque_s(g.nwx);
     g.nwy = opaque_s(g.nwy);
-    for (int r = tid; r < m; r += kThreads) tab[r] = window_token(g, win, r);
+    if (hf == 0 && kvalid) tab[key] = window_token(g, win, key);
   };
   // Q and dO loads of query tile it into buffer it: 1 KB instructions i0,
   // i0 + 1, ..., i0 + n - 1 of the tile
@@ -925,28 +929,26 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
   auto tiles = [&](int it, int64_t base, const int32_t* tab) __attribute__((always_inline)) {
     tile_part(it, wv * Q::kIpw, Q::kIpw, base, tab);
   };
-  // log2-scale log-sum-exp and Dv of tile it's queries (threads < kQ); a
-  // missing query gets P = 0
-  auto vec = [&](int it, int bh, const int32_t* tab, float& lx, float& dvx)
-      __attribute__((always_inline)) {
-    if (tid < kQ) {
-      const int q = it * kQ + tid;
-      const bool ok = q < m;
-      const int64_t idx = (int64_t)bh * p.n + tab[ok ? q : m - 1];
-      lx = ok ? p.lse[idx] * kLog2e : INFINITY;
-      dvx = ok ? p.dvec[idx] : 0.0f;
+  // The wave's 32 queries (its keys' tokens): lanes 0-31 the log2-scale
+  // log-sum-exp, lanes 32-63 Dv; a missing query gets P = 0.
+  auto vec = [&](int bh, const int32_t* tab) __attribute__((always_inline)) {
+    float x = hf ? 0.0f : INFINITY;
+    if (kvalid) {
+      const int64_t idx = (int64_t)bh * p.n + tab[key];
+      x = hf ? p.dvec[idx] : p.lse[idx] * kLog2e;
     }
+    return x;
   };
-  auto put = [&](int j, int it, float lx, float dvx) __attribute__((always_inline)) {
-    if (tid < kQ) {
-      float* sl = reinterpret_cast<float*>(slb(j, it));
-      sl[(tid / kBlk) * 64 + perm32(tid % kBlk)] = lx;
-      sl[(tid / kBlk) * 64 + 32 + perm32(tid % kBlk)] = dvx;
-    }
+  // query `key` is row key % 64 of tile key / 64: block (wave & 1) of tile
+  // wave / 2; tiles past the window's last hold only missing queries
+  auto put = [&](int j, float x) __attribute__((always_inline)) {
+    float* sl = reinterpret_cast<float*>(slb(j, wave >> 1));
+    sl[(wave & 1) * 64 + hf * 32 + perm32(l32)] = x;
   };
   u32x4 kreg[T::QS], vreg[T::QS];   // this lane's K and V rows (B operands)
+  // (a key past the window's end loads token 0's rows, never stored)
   auto rows = [&](int64_t base, const int32_t* tab) __attribute__((always_inline)) {
-    const uint32_t koff = (uint32_t)tab[kcl] * stb;
+    const uint32_t koff = kvalid ? (uint32_t)tab[key] * stb : 0u;
     const Rsrc rk = make_rsrc(p.k + base), rv = make_rsrc(p.v + base);
 #pragma unroll
     for (int s = 0; s < T::QS; ++s) {
@@ -967,10 +969,10 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
   };
 
   // unit 0: its table, rows, tiles, lse and Dv
-  build_table(tab_of(0), win_of(0));
+  build_rows(tab_of(0), win_of(0));
   if (tid < kNB) cnt[tid] = 0;
-  __syncthreads();
-  float lxs[kNB], dvs[kNB];
+  __syncthreads();   // the whole table, for the tile loads
+  float lsd;         // the next unit's lse / Dv of this lane (vec)
   {
     const int bh = bh_of(0);
     const int64_t base = slice_base(p, bh);
@@ -978,9 +980,7 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
 #pragma unroll
     for (int it = 0; it < kNB; ++it)
       if (it < nit) tiles(it, base, tab_of(0));
-#pragma unroll
-    for (int it = 0; it < kNB; ++it)
-      if (it < nit) vec(it, bh, tab_of(0), lxs[it], dvs[it]);
+    lsd = vec(bh, tab_of(0));
   }
   for (int j = 0; j < J; ++j) {
     const bool has_next = j + 1 < J;
@@ -988,15 +988,13 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
     const int bh = bh_of(j);
     const int64_t base = slice_base(p, bh);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of the unit have landed
-#pragma unroll
-    for (int it = 0; it < kNB; ++it)
-      if (it < nit) put(j, it, lxs[it], dvs[it]);
+    put(j, lsd);
     // Every wave's tiles, lse and Dv are in LDS; every wave is done with the
     // previous unit (its table and lse / Dv slots are free for the next unit's).
     __syncthreads();
     const int bhn = has_next ? bh_of(j + 1) : bh;
     const int64_t basen = slice_base(p, bhn);
-    if (has_next) build_table(tab_of(j + 1), win_of(j + 1));
+    if (has_next) build_rows(tab_of(j + 1), win_of(j + 1));
     {  // pass 0: dV
       f32x16 acc[T::DB];
 #pragma unroll
@@ -1023,8 +1021,8 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
           // This wave's reads of buffer it precede the count (LDS operations
           // of a wave run in order; the empty asm keeps the compiler from
           // moving them past it).  The wave whose count completes the tile
-          // loads all of it; the next table was built before the unit's
-          // pass 0 by every wave, whose counts it has seen.
+          // loads all of it; every wave built its rows of the next table
+          // before its pass 0, and so before its count.
           asm volatile("" ::: "memory");
           int old = 0;
           if (lane == 0)
@@ -1054,10 +1052,8 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
         __syncthreads();   // every wave is done with the last buffer
         tiles(nit - 1, basen, tab_of(j + 1));
       }
-      rows(basen, tab_of(j + 1));
-#pragma unroll
-      for (int it = 0; it < kNB; ++it)
-        if (it < nit) vec(it, bhn, tab_of(j + 1), lxs[it], dvs[it]);
+      rows(basen, tab_of(j + 1));   // this wave's own rows of the next table
+      lsd = vec(bhn, tab_of(j + 1));
     }
   }
 }
