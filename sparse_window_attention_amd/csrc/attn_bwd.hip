@@ -211,6 +211,15 @@ __global__ void __launch_bounds__(256) bwd_dvec_kernel(BwdParams p) {
   if (c == 0) p.dvec[row] = s;
 }
 
+// A wave-uniform pointer held in vector registers, read into scalar ones.
+template <class P>
+__device__ __forceinline__ P* uniform_ptr(P* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- dq
 // dQ with the key tiles loaded straight into LDS: 64 keys per iteration, K
 // and V tiles row-major (16-byte chunks XOR-swizzled per row), K rows and V
@@ -320,7 +329,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, BASA_DQ_LV(i), 16, off, 0, 0, 0);
       }
     } else if (memT) {
-      const Rsrc rk = make_rsrc(kmem), rvs = make_rsrc(vmem);
+      // scalar copies: the mixed-tile path keeps kmem / vmem in vector
+      // registers, and a resource built from those would wrap every load in
+      // a loop over its lanes' values
+      const Rsrc rk = make_rsrc(uniform_ptr(kmem)), rvs = make_rsrc(uniform_ptr(vmem));
 #pragma unroll
       for (int i = 0; i < Q::kIpw; ++i) {
         const uint32_t off = (uint32_t)(k0 - p.m + r[i]) * (D * 2) + cb[i];
