@@ -863,7 +863,6 @@ __device__ __forceinline__ void dkdv_res_body(const BwdParams& p) {
   constexpr int PF = BASA_BWD_RES_PREFETCH;
   using T = BT<D>;
   using Q = DqDma<D, NW>;
-  constexpr int kThreads = NW * 64;
   constexpr int CPR = Q::CPR, TB = Q::kTileB;
   constexpr int kQ = Q::kKeys;                 // queries per tile
   constexpr int kMaxM = NW * 32;               // window tokens at most (keys of the unit)
