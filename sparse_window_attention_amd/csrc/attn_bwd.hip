@@ -772,13 +772,10 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int blk) {
       const unsigned char* sqt = buf(it);   // Q tile, dO tile, lse and Dv
       if constexpr (RES) {
         dkdv_blocks<D, NW, PS, 0, 2>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
-      } else if constexpr (MEM) {
+      } else {
         // the interleaved order fits beside the next tile's load state only
         // with the addresses formed per tile
         dkdv_blocks<D, NW, PS, 0, 2, true>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
-      } else {
-        dkdv_blocks<D, NW, PS, 0, 1>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
-        dkdv_blocks<D, NW, PS, 1, 1>(sqt, sqt + 2 * TB, kreg, vreg, acc, c1, l32, hf, lane);
       }
       if constexpr (!RES) {
         if (it + 1 < nit) put(it + 1);
