@@ -1082,18 +1082,37 @@ __global__ void __launch_bounds__(kNW * 64, 1) bwd_dkdv_res_kernel(BwdParams p) 
 // ---------------------------------------------------------------- memsum
 template <int D>
 __global__ void __launch_bounds__(256) bwd_memsum_kernel(BwdParams p, float inv_cell) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over bh, g, d
+  // four consecutive d of one (b*h, memory key) per thread (G * D is a
+  // multiple of 4, the buffers 16-byte aligned); the loads of four query
+  // chunks go out together, and each element still sums the chunks in order
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // over bh, g, d
   const int64_t per = (int64_t)p.G * D;
   if (i >= (int64_t)p.batch_heads * per) return;
   const int64_t bh = i / per, rest = i - bh * per;
-  float sk = 0.0f, sv = 0.0f;
-  for (int c = 0; c < p.nqc; ++c) {
-    const int64_t j = (bh * p.nqc + c) * per + rest;
-    sk += p.pk[j];
-    sv += p.pv[j];
+  const f32x4* pk = reinterpret_cast<const f32x4*>(p.pk + bh * p.nqc * per + rest);
+  const f32x4* pv = reinterpret_cast<const f32x4*>(p.pv + bh * p.nqc * per + rest);
+  const int64_t cs = per / 4;   // one query chunk's partials, in 4-float steps
+  f32x4 sk = {}, sv = {};
+  int c = 0;
+  for (; c + 4 <= p.nqc; c += 4) {
+    f32x4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = pk[(c + u) * cs];
+      b[u] = pv[(c + u) * cs];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sk += a[u];
+      sv += b[u];
+    }
   }
-  p.gk[i] = sk * p.scale * inv_cell;
-  p.gv[i] = sv * inv_cell;
+  for (; c < p.nqc; ++c) {
+    sk += pk[c * cs];
+    sv += pv[c * cs];
+  }
+  *reinterpret_cast<f32x4*>(p.gk + i) = sk * p.scale * inv_cell;
+  *reinterpret_cast<f32x4*>(p.gv + i) = sv * inv_cell;
 }
 
 template <typename K>
@@ -1156,7 +1175,7 @@ int launch_d(const BwdParams& p, hipStream_t stream) {
   if (p.G > 0) {
     if ((rc = launch_dkdv<D, true>(p, stream))) return rc;
     const int64_t total = (int64_t)p.batch_heads * p.G * D;
-    hipLaunchKernelGGL((bwd_memsum_kernel<D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_memsum_kernel<D>), dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0,
                        stream, p, 1.0f / (float)(p.pt * p.py * p.px));
     if (hipGetLastError() != hipSuccess) return BASA_ERR_HIP;
   }
